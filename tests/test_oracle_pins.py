@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test ties an oracle function to something other than itself: values the
+pages print (byte counts), hand-worked cases, closed forms, exact rational
+arithmetic of the page's FMA rearrangement, or brute force on tiny inputs.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_kv(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            out[k] = v
+    return out
+
+
+# --------------------------------------------------------------------------
+# Layout byte counts printed on the pages
+# --------------------------------------------------------------------------
+
+def test_layout_sizes_match_printed_values():
+    rows = {}
+    with open(os.path.join(GOLDEN, "layout_sizes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, val, unit, tol, *_ = line.split()
+                rows[name] = (float(val), float(tol))
+    e4 = oracle.expert_bytes(4096, 1024, 4)
+    e2 = oracle.expert_bytes(4096, 1024, 2)
+    assert e4 == 7_077_888 and e2 == 3_932_160
+    got = {
+        "expert_4bit_MiB": e4 / 2 ** 20,
+        "io_per_token_2bit_MB": 60 * 4 * e2 / 1e6,
+        "total_2bit_GB": 60 * 512 * e2 / 1e9,
+    }
+    for k, (val, tol) in rows.items():
+        assert abs(got[k] - val) <= tol * val, (k, got[k], val)
+
+
+def test_layout_offsets_are_ordered_and_aligned():
+    off = oracle.expert_offsets(4096, 1024, 4)
+    names = ["gate_codes", "up_codes", "down_codes", "gate_sb", "up_sb", "down_sb"]
+    pos = 0
+    for n in names:
+        o, s = off[n]
+        assert o == pos and o % 256 == 0
+        pos += s
+    assert off["total"] == pos
+    # other group multiples
+    assert oracle.expert_bytes(128, 64, 2) == 2 * 64 * 128 // 4 + 128 * 64 // 4 + 4 * (2 * 64 * 2 + 128)
+
+
+# --------------------------------------------------------------------------
+# Dequantisation: hand-built cases
+# --------------------------------------------------------------------------
+
+def _hexrow(words):
+    return np.frombuffer(bytes.fromhex("".join(words)), dtype=np.uint8)
+
+
+def test_dequant_handmade_4bit():
+    g = _golden_kv("dequant_handmade.txt")
+    cols = int(g["A.cols"][0])
+    codes = np.stack([_hexrow(g["A.row0"]), _hexrow(g["A.row1"])])
+    sb = np.array([[int(g["A.sb0"][0], 16)], [int(g["A.sb1"][0], 16)]], dtype=np.uint32)
+    W = oracle.dequant(codes, sb, cols, 4)
+    np.testing.assert_array_equal(W[0, :16], [float(v) for v in g["A.W0_first16"]])
+    np.testing.assert_array_equal(W[1, :4], [float(v) for v in g["A.W1_first4"]])
+    y = oracle.qgemv(codes, sb, np.ones(cols), 4)
+    np.testing.assert_array_equal(y, [float(v) for v in g["A.y_ones"]])
+
+
+def test_dequant_handmade_2bit_two_groups():
+    g = _golden_kv("dequant_handmade.txt")
+    cols = int(g["B.cols"][0])
+    codes = _hexrow(g["B.row0"])[None, :]
+    sb = np.array([[int(v, 16) for v in g["B.sb0"]]], dtype=np.uint32)
+    W = oracle.dequant(codes, sb, cols, 2)
+    np.testing.assert_array_equal(W[0, :4], [float(v) for v in g["B.W0_first4"]])
+    np.testing.assert_array_equal(W[0, 64:68], [float(v) for v in g["B.W0_64_to_67"]])
+    np.testing.assert_array_equal(oracle.qgemv(codes, sb, np.ones(cols), 2), [float(g["B.y_ones"][0])])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_unit_vector_picks_one_column(bits):
+    """x = e_k returns column k of W: catches bit-order and transposition mistakes."""
+    rng = np.random.default_rng(7)
+    rows, cols = 5, 128
+    codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
+    sb = np.zeros((rows, cols // 64), dtype=np.uint32) | np.uint32(0x3F80)  # scale 1, bias 0
+    for k in (0, 1, 2, 3, 5, 63, 64, 127):
+        x = np.zeros(cols)
+        x[k] = 1.0
+        y = oracle.qgemv(codes, sb, x, bits)
+        byte = codes[:, (k * bits) // 8].astype(np.int64)
+        expect = (byte >> ((k * bits) % 8)) & ((1 << bits) - 1)
+        np.testing.assert_array_equal(y, expect.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_unit_scale_zero_bias_is_integer_matmul(bits):
+    """scale 1, bias 0: the GEMV is an integer matrix times an integer vector, exact."""
+    rng = np.random.default_rng(11)
+    rows, cols = 9, 192
+    q = rng.integers(0, 1 << bits, size=(rows, cols))
+    packed = np.zeros((rows, cols * bits // 8), dtype=np.uint8)
+    per = 8 // bits
+    for k in range(cols):  # pack by hand with the documented rule
+        packed[:, k // per] |= (q[:, k] << ((k % per) * bits)).astype(np.uint8)
+    sb = np.full((rows, cols // 64), 0x3F80, dtype=np.uint32)
+    x = rng.integers(-1000, 1000, size=cols)
+    y = oracle.qgemv(packed, sb, x.astype(np.float64), bits)
+    np.testing.assert_array_equal(y, (q @ x).astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_constant_codes_closed_form(bits):
+    """All codes c, constant scale s and bias b: y_n = (c*s + b) * sum(x)."""
+    rows, cols = 3, 256
+    c = (1 << bits) - 2
+    byte = 0
+    for j in range(8 // bits):
+        byte |= c << (j * bits)
+    codes = np.full((rows, cols * bits // 8), byte, dtype=np.uint8)
+    s_bits, b_bits = 0x3E00, 0xBD00          # 0.125 and -0.03125
+    sb = np.full((rows, cols // 64), s_bits | (b_bits << 16), dtype=np.uint32)
+    x = np.random.default_rng(3).standard_normal(cols)
+    y = oracle.qgemv(codes, sb, x, bits)
+    np.testing.assert_allclose(y, (c * 0.125 - 0.03125) * x.sum() * np.ones(rows), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# The FMA rearrangement of the page is an identity (exact rational arithmetic)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_fma_rearrangement_identity_exact(bits):
+    """Sum over k of (q*s + b)*x  ==  sum of fma(q, s*x, b*x)  ==  per-group
+    s*sum(q*x) + b*sum(x), exactly in rationals; the oracle's float64 value
+    agrees to rounding.  Source: "flash-moe 소개", section
+    "FMA 최적화 역양자화 커널" (the (nibble*scale+bias)*x -> fma(nibble, scale*x,
+    bias*x) rearrangement)."""
+    rng = np.random.default_rng(5 + bits)
+    rows, cols = 2, 128
+    codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
+    s16 = rng.integers(0x3A00, 0x3D00, size=(rows, cols // 64)).astype(np.uint32)
+    b16 = rng.integers(0xBC00, 0xBD00, size=(rows, cols // 64)).astype(np.uint32)
+    sb = s16 | (b16 << 16)
+    x = rng.standard_normal(cols)
+
+    def bf(u):
+        return Fraction(float(np.array([u << 16], dtype=np.uint32).view(np.float32)[0]))
+
+    per = 8 // bits
+    for n in range(rows):
+        q = [(int(codes[n, k // per]) >> ((k % per) * bits)) & ((1 << bits) - 1) for k in range(cols)]
+        xs = [Fraction(float(v)) for v in x]
+        s = [bf(int(s16[n, g])) for g in range(cols // 64)]
+        b = [bf(int(b16[n, g])) for g in range(cols // 64)]
+        naive = sum((q[k] * s[k // 64] + b[k // 64]) * xs[k] for k in range(cols))
+        fma_form = sum(q[k] * (s[k // 64] * xs[k]) + (b[k // 64] * xs[k]) for k in range(cols))
+        grouped = sum(s[g] * sum(q[k] * xs[k] for k in range(64 * g, 64 * g + 64))
+                      + b[g] * sum(xs[64 * g:64 * g + 64]) for g in range(cols // 64))
+        assert naive == fma_form == grouped
+        y = oracle.qgemv(codes[n:n + 1], sb[n:n + 1], x, bits)[0]
+        assert abs(y - float(naive)) <= 1e-13 * max(1.0, abs(float(naive)))
+
+
+# --------------------------------------------------------------------------
+# Router, softmax and top-K
+# --------------------------------------------------------------------------
+
+def _bf16(v):
+    return (np.array(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_router_handmade_with_ties():
+    # E=6, H=2, x=(1,1): logits [0.5, 1, 2, -1, 0.5, 1] (all exact in bf16)
+    Wr = _bf16([[0.5, 0.0], [1.0, 0.0], [0.0, 2.0], [-1.0, 0.0], [0.25, 0.25], [0.5, 0.5]])
+    logits = oracle.router_logits(Wr, np.array([1.0, 1.0]))
+    np.testing.assert_array_equal(logits, [0.5, 1, 2, -1, 0.5, 1])
+    idx, w = oracle.router_topk(logits, 4)
+    assert list(idx) == [2, 1, 5, 0]          # ties go to the lower index
+    idx2, w2 = oracle.router_topk(logits, 2)
+    assert list(idx2) == [2, 1]
+    e = math.e
+    np.testing.assert_allclose(w2, [e / (1 + e), 1 / (1 + e)], rtol=1e-15)
+
+
+def _brute_force_topk_set(logits, k):
+    p = np.exp(logits - logits.max())
+    p /= p.sum()
+    best, best_mass = None, -1.0
+    for subset in itertools.combinations(range(logits.size), k):
+        mass = float(sum(p[list(subset)]))
+        if mass > best_mass:
+            best, best_mass = subset, mass
+    return set(best), p
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (6, 2), (8, 4), (10, 3), (10, 10)])
+def test_topk_brute_force(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    for _ in range(20):
+        logits = rng.standard_normal(E) * 3
+        idx, w = oracle.router_topk(logits, k)
+        best, p = _brute_force_topk_set(logits, k)
+        assert set(idx.tolist()) == best
+        assert all(logits[idx[i]] >= logits[idx[i + 1]] for i in range(k - 1))
+        assert abs(w.sum() - 1.0) < 1e-15
+        np.testing.assert_allclose(w, p[idx] / p[idx].sum(), rtol=1e-13)
+        # invariance to a shift of every logit
+        idx_s, w_s = oracle.router_topk(logits + 123.0, k)
+        assert list(idx_s) == list(idx)
+        np.testing.assert_allclose(w_s, w, rtol=1e-12)
+
+
+def test_topk_decides_in_float32():
+    # two logits that differ in float64 but round to the same float32: a tie,
+    # broken towards the lower index, as the fp32 kernel does
+    a = 1.0
+    b = 1.0 + 2.0 ** -30
+    assert np.float32(a) == np.float32(b)
+    idx, _ = oracle.router_topk(np.array([0.0, a, b, -1.0]), 1)
+    assert list(idx) == [1]
+    idx64, _ = oracle.router_topk(np.array([0.0, a, b, -1.0]), 1, decide_in=None)
+    assert list(idx64) == [2]
+
+
+# --------------------------------------------------------------------------
+# SwiGLU, sigmoid, expert FFN, combine
+# --------------------------------------------------------------------------
+
+def test_silu_sigmoid_special_values():
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    np.testing.assert_allclose(oracle.silu(1.0), 1.0 / (1.0 + math.exp(-1.0)), rtol=1e-15)
+    # silu(z) - silu(-z) = z
+    z = np.linspace(-5, 5, 11)
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, atol=1e-14)
+
+
+def _const_expert_block(H, I, bits, gate, up, down):
+    """Expert whose three matrices are constant: (code, scale_bits, bias_bits)."""
+    blk = np.zeros(oracle.expert_bytes(H, I, bits), dtype=np.uint8)
+    off = oracle.expert_offsets(H, I, bits)
+    for name, (c, s, b) in (("gate", gate), ("up", up), ("down", down)):
+        o, n = off[name + "_codes"]
+        byte = 0
+        for j in range(8 // bits):
+            byte |= c << (j * bits)
+        blk[o:o + n] = byte
+        o, n = off[name + "_sb"]
+        blk[o:o + n] = np.full(n // 4, s | (b << 16), dtype=np.uint32).view(np.uint8)
+    return blk
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_expert_ffn_closed_form(bits):
+    """Constant matrices: gate W=1, up W=2, down W=0.5 and sum(x)=1 give
+    a = 1, u = 2, h = silu(1)*2, y_n = I * 0.5 * h = I*silu(1).  A swap of
+    gate and up (silu on the up projection) would give I*silu(2)/2 instead."""
+    H, I = 128, 64
+    gate = (2, 0x3F00, 0x0000)      # 2*0.5 + 0 = 1
+    up = (1, 0x3F80, 0x3F80)        # 1*1 + 1 = 2
+    down = (3, 0x3E80, 0xBE80)      # 3*0.25 - 0.25 = 0.5
+    blk = _const_expert_block(H, I, bits, gate, up, down)
+    x = np.full(H, 1.0 / H)
+    y, mid = oracle.expert_ffn(blk, x, H, I, bits, return_intermediates=True)
+    np.testing.assert_allclose(mid["a"], 1.0, rtol=1e-14)
+    np.testing.assert_allclose(mid["u"], 2.0, rtol=1e-14)
+    np.testing.assert_allclose(y, I * oracle.silu(1.0), rtol=1e-13)
+    assert abs(I * oracle.silu(2.0) / 2 - I * oracle.silu(1.0)) > 1.0
+
+
+def test_combine_special_cases():
+    H, K = 8, 3
+    rng = np.random.default_rng(2)
+    ys = rng.standard_normal((K, H))
+    y_sh = rng.standard_normal(H)
+    x = rng.standard_normal(H)
+    r = rng.standard_normal(H)
+    g0 = np.zeros(H, dtype=np.uint16)                # g = 0 -> gamma = 1/2
+    out = oracle.combine_residual_gate(ys, np.zeros(K), y_sh, g0, x, r)
+    np.testing.assert_allclose(out, r + 0.5 * y_sh, rtol=1e-15)
+    out1 = oracle.combine_residual_gate(ys[:1], np.ones(1), np.zeros(H), g0, x, r)
+    np.testing.assert_allclose(out1, r + ys[0], rtol=1e-15)
+    # a large gate saturates the sigmoid: gamma -> 1 ; negative -> 0
+    big = _bf16(np.full(H, 64.0))
+    xs = np.ones(H)
+    np.testing.assert_allclose(oracle.combine_residual_gate(ys, np.zeros(K), y_sh, big, xs, r),
+                               r + y_sh, rtol=1e-12)
+    np.testing.assert_allclose(oracle.combine_residual_gate(ys, np.zeros(K), y_sh, big, -xs, r),
+                               r, rtol=1e-12, atol=1e-12)
+    w = np.array([0.5, 0.25, 0.25])
+    out2 = oracle.combine_residual_gate(ys, w, y_sh, g0, x, r)
+    np.testing.assert_allclose(out2, r + 0.5 * ys[0] + 0.25 * ys[1] + 0.25 * ys[2] + 0.5 * y_sh,
+                               rtol=1e-14)
+
+
+def test_rmsnorm_closed_forms():
+    H = 16
+    w = np.linspace(0.9, 1.1, H)
+    for c in (1.0, -3.0, 1e-4):
+        out = oracle.rmsnorm(np.full(H, c), w, 1e-6)
+        np.testing.assert_allclose(out, c / math.sqrt(c * c + 1e-6) * w, rtol=1e-14)
+    v = np.random.default_rng(4).standard_normal(H)
+    # eps = 0: scale invariance and unit RMS with w = 1
+    np.testing.assert_allclose(oracle.rmsnorm(7.5 * v, w, 0.0), oracle.rmsnorm(v, w, 0.0), rtol=1e-14)
+    o = oracle.rmsnorm(v, np.ones(H), 0.0)
+    assert abs(math.sqrt(np.mean(o * o)) - 1.0) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Layer-level structure
+# --------------------------------------------------------------------------
+
+def _small_layer(bits, E=6, H=128, I=64, seed=1):
+    rng = np.random.default_rng(seed)
+    nb = oracle.expert_bytes(H, I, bits)
+    off = oracle.expert_offsets(H, I, bits)
+    blocks = []
+    for _ in range(E + 1):
+        blk = rng.integers(0, 256, size=nb, dtype=np.uint8)
+        for name in ("gate_sb", "up_sb", "down_sb"):
+            o, n = off[name]
+            s = rng.integers(0x3A00, 0x3C80, size=n // 4).astype(np.uint32)
+            b = rng.integers(0xBC00, 0xBD00, size=n // 4).astype(np.uint32)
+            blk[o:o + n] = (s | (b << 16)).view(np.uint8)
+        blocks.append(blk)
+    router = _bf16(rng.standard_normal((E, H)) * 0.1)
+    gate = _bf16(rng.standard_normal(H) * 0.1)
+    return blocks[:E], blocks[E], router, gate
+
+
+def test_moe_layer_zero_experts_is_residual():
+    """Experts whose weights are all zero contribute nothing: out = residual."""
+    H, I, bits = 128, 64, 4
+    zero = np.zeros(oracle.expert_bytes(H, I, bits), dtype=np.uint8)
+    router = _bf16(np.random.default_rng(0).standard_normal((5, H)))
+    x = np.random.default_rng(1).standard_normal(H)
+    r = np.random.default_rng(2).standard_normal(H)
+    out = oracle.moe_layer(lambda e: zero, zero, router, np.zeros(H, np.uint16), x, r, H, I, bits, 2)
+    np.testing.assert_array_equal(out, r)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_moe_layer_matches_its_parts(bits):
+    """The layer uses the selected experts with their renormalised weights and
+    gates only the shared expert (checked against the parts computed one by one)."""
+    H, I, K = 128, 64, 2
+    experts, shared, router, gate = _small_layer(bits)
+    x = np.random.default_rng(9).standard_normal(H)
+    out, d = oracle.moe_layer(lambda e: experts[e], shared, router, gate, x, x, H, I, bits, K,
+                              return_details=True)
+    logits = oracle.bf16_bits_to_f64(router) @ x
+    order = np.argsort(-logits, kind="stable")[:K]
+    assert list(d["idx"]) == list(order)
+    p = np.exp(logits - logits.max())
+    w = p[order] / p[order].sum()
+    gamma = 1 / (1 + np.exp(-(oracle.bf16_bits_to_f64(gate) @ x)))
+    expect = x + sum(w[i] * oracle.expert_ffn(experts[order[i]], x, H, I, bits) for i in range(K)) \
+        + gamma * oracle.expert_ffn(shared, x, H, I, bits)
+    np.testing.assert_allclose(out, expect, rtol=1e-12)
+
+
+def test_batched_rows_equal_single_token():
+    H, I, bits, K = 128, 64, 4, 2
+    experts, shared, router, gate = _small_layer(bits, seed=3)
+    X = np.random.default_rng(5).standard_normal((3, H))
+    out = oracle.moe_layer_batched(lambda e: experts[e], shared, router, gate, X, X, H, I, bits, K)
+    for t in range(3):
+        np.testing.assert_array_equal(
+            out[t], oracle.moe_layer(lambda e: experts[e], shared, router, gate, X[t], X[t],
+                                     H, I, bits, K))
+
+
+def test_stack_of_zero_layers_keeps_h():
+    H, I, bits = 128, 64, 2
+    zero = np.zeros(oracle.expert_bytes(H, I, bits), dtype=np.uint8)
+    router = _bf16(np.random.default_rng(0).standard_normal((4, H)))
+    layers = [dict(get_expert=lambda e: zero, shared_block=zero, router=router,
+                   shared_gate=np.zeros(H, np.uint16), norm_w=np.ones(H)) for _ in range(3)]
+    h0 = np.random.default_rng(8).standard_normal(H)
+    np.testing.assert_array_equal(oracle.moe_stack(layers, h0, H, I, bits, 2), h0)
+
+
+def test_stack_feeds_normalised_input():
+    """One layer with constant experts: x = rmsnorm(h0) enters the experts,
+    h0 (not x) is the residual."""
+    H, I, bits = 128, 64, 4
+    blk = _const_expert_block(H, I, bits, (2, 0x3F00, 0), (1, 0x3F80, 0x3F80), (3, 0x3E80, 0xBE80))
+    router = _bf16(np.zeros((2, H)))
+    h0 = np.full(H, 3.0)
+    w = np.full(H, 1.0 / H)   # x = rmsnorm(h0) * w = (3/sqrt(9+eps)) / H per entry, sum(x) ~ 1
+    layer = dict(get_expert=lambda e: blk, shared_block=blk, router=router,
+                 shared_gate=np.zeros(H, np.uint16), norm_w=w)
+    out = oracle.moe_stack([layer], h0, H, I, bits, 1)
+    S = 3.0 / math.sqrt(9.0 + 1e-6)        # sum of x
+    y = I * 0.5 * 2.0 * S * oracle.silu(S)  # constant-expert output for sum(x) = S
+    np.testing.assert_allclose(out, h0 + y + 0.5 * y, rtol=1e-12)
