@@ -1,0 +1,282 @@
+"""Python binding of libqmoe (batch-1 quantized MoE expert forward on MI355X).
+
+A thin ctypes layer over the C ABI declared in ``include/qmoe.h``: the functions
+here have the same names as the C entry points, take torch tensors that live
+on the GPU, marshal pointers and the current HIP stream, and raise
+``QmoeError`` on a non-zero status.  Every step of the computation runs in the
+library's HIP kernels; nothing here computes.  Importing this module fails
+loudly if the library has not been built (run ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950); there is no fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+QMOE_OK, QMOE_EINVAL, QMOE_ESHAPE, QMOE_EALIGN, QMOE_EWORKSPACE, QMOE_EHIP, QMOE_EUNSUPPORTED = \
+    0, -1, -2, -3, -4, -5, -6
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_lib.qmoe_strerror(status).decode()} ({status}): "
+                         f"{_lib.qmoe_last_error().decode()}")
+
+
+class ExpertOffsets(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("gate_codes", "up_codes", "down_codes", "gate_sb", "up_sb", "down_sb", "total")]
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("sb", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class ExpertPoolC(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_int64),
+                ("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+class LayerC(ctypes.Structure):
+    _fields_ = [("routed", ExpertPoolC), ("shared", ExpertPoolC), ("router", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p), ("top_k", ctypes.c_int32)]
+
+
+_vp, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "qmoe_expert_layout": ([_i32, _i32, _i32, ctypes.POINTER(ExpertOffsets)], ctypes.c_int),
+    "qgemv_w4": ([ctypes.POINTER(QMat), _vp, _vp, _vp], ctypes.c_int),
+    "qgemv_w2": ([ctypes.POINTER(QMat), _vp, _vp, _vp], ctypes.c_int),
+    "moe_router_topk": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "expert_ffn_swiglu": ([ctypes.POINTER(ExpertPoolC), _vp, _i32, _vp, _vp, _vp, _sz, _vp],
+                          ctypes.c_int),
+    "qmoe_ffn_workspace_bytes": ([ctypes.POINTER(ExpertPoolC), _i32], _sz),
+    "moe_combine_residual_gate": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp], ctypes.c_int),
+    "moe_layer_forward": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                          ctypes.c_int),
+    "moe_layer_forward_batched": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                                   _vp], ctypes.c_int),
+    "qmoe_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
+    "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
+    "qmoe_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "qmoe_last_error": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+def _check(rc, where):
+    if rc != QMOE_OK:
+        raise QmoeError(rc, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# data structures
+# ---------------------------------------------------------------------------
+
+def qmoe_expert_layout(hidden: int, inter: int, bits: int) -> dict:
+    o = ExpertOffsets()
+    _check(_lib.qmoe_expert_layout(hidden, inter, bits, ctypes.byref(o)), "qmoe_expert_layout")
+    return {n: getattr(o, n) for n, _ in ExpertOffsets._fields_}
+
+
+class ExpertPool:
+    """E expert blocks resident in one uint8 GPU tensor, expert e at byte e*stride."""
+
+    def __init__(self, buf: torch.Tensor, num_experts: int, hidden: int, inter: int, bits: int,
+                 stride: int | None = None):
+        lay = qmoe_expert_layout(hidden, inter, bits)
+        self.stride = stride if stride is not None else (lay["total"] + 255) // 256 * 256
+        if buf.dtype != torch.uint8 or buf.numel() < self.stride * (num_experts - 1) + lay["total"]:
+            raise ValueError("pool buffer must be uint8 and hold every expert")
+        self.buf, self.num_experts, self.hidden, self.inter, self.bits = buf, num_experts, hidden, inter, bits
+        self.layout = lay
+
+    @staticmethod
+    def allocate(num_experts, hidden, inter, bits, device="cuda"):
+        lay = qmoe_expert_layout(hidden, inter, bits)
+        stride = (lay["total"] + 255) // 256 * 256
+        buf = torch.empty(stride * num_experts, dtype=torch.uint8, device=device)
+        return ExpertPool(buf, num_experts, hidden, inter, bits, stride)
+
+    def c(self) -> ExpertPoolC:
+        return ExpertPoolC(self.buf.data_ptr(), self.stride, self.num_experts, self.hidden,
+                           self.inter, self.bits)
+
+    def expert_bytes(self, e: int) -> torch.Tensor:
+        o = e * self.stride
+        return self.buf[o:o + self.layout["total"]]
+
+
+class Layer:
+    """One MoE layer: routed pool, shared expert (pool of 1), router and shared gate."""
+
+    def __init__(self, routed: ExpertPool, shared: ExpertPool, router: torch.Tensor,
+                 shared_gate: torch.Tensor, top_k: int):
+        self.routed, self.shared, self.router, self.shared_gate, self.top_k = \
+            routed, shared, router, shared_gate, top_k
+        _ptr(router, None, "router")          # bf16 bits (torch.int16 or torch.bfloat16)
+        _ptr(shared_gate, None, "shared_gate")
+
+    def c(self) -> LayerC:
+        return LayerC(self.routed.c(), self.shared.c(), self.router.data_ptr(),
+                      self.shared_gate.data_ptr(), self.top_k)
+
+
+def qmoe_workspace_bytes(layer: Layer, T: int = 1) -> int:
+    return int(_lib.qmoe_workspace_bytes(ctypes.byref(layer.c()), T))
+
+
+def qmoe_ffn_workspace_bytes(pool: ExpertPool, n: int) -> int:
+    return int(_lib.qmoe_ffn_workspace_bytes(ctypes.byref(pool.c()), n))
+
+
+def alloc_workspace(layer: Layer, T: int = 1) -> torch.Tensor:
+    """A zero-filled workspace (the fused layer kernel requires zero on first use)."""
+    n = qmoe_workspace_bytes(layer, T)
+    if n == 0:
+        raise ValueError("bad layer or batch size")
+    return torch.zeros(n, dtype=torch.uint8, device=layer.routed.buf.device)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def _qgemv(fn, bits, codes, sb, x, y, rows, cols):
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=x.device)
+    m = QMat(_ptr(codes, None, "codes").value, _ptr(sb, None, "sb").value, rows, cols)
+    _check(fn(ctypes.byref(m), _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"), _stream()),
+           f"qgemv_w{bits}")
+    return y
+
+
+def qgemv_w4(codes, sb, x, y=None):
+    """y = W x for a 4-bit matrix (codes uint8 [rows][cols/2], sb int32/uint32 [rows][cols/64])."""
+    return _qgemv(_lib.qgemv_w4, 4, codes, sb, x, y, codes.shape[0], x.numel())
+
+
+def qgemv_w2(codes, sb, x, y=None):
+    """y = W x for a 2-bit matrix (codes uint8 [rows][cols/4])."""
+    return _qgemv(_lib.qgemv_w2, 2, codes, sb, x, y, codes.shape[0], x.numel())
+
+
+def moe_router_topk(router, x, k, logits=None, idx=None, w=None):
+    """Router GEMV + softmax top-k for x [T][H]; returns (idx int32 [T][k], w [T][k], logits)."""
+    x2 = x.reshape(-1, router.shape[1])
+    T, H = x2.shape
+    E = router.shape[0]
+    dev = x.device
+    logits = logits if logits is not None else torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = idx if idx is not None else torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(T, k, dtype=torch.float32, device=dev)
+    _check(_lib.moe_router_topk(_ptr(router, None, "router"), _ptr(x2, torch.float32, "x"), T, H, E, k,
+                                _ptr(logits, torch.float32, "logits"), _ptr(idx, torch.int32, "idx"),
+                                _ptr(w, torch.float32, "w"), _stream()), "moe_router_topk")
+    return idx, w, logits
+
+
+def expert_ffn_swiglu(pool: ExpertPool, expert_idx, x, y=None, ws=None):
+    """y[i] = D_e(silu(G_e x) * U_e x) for e = expert_idx[i] (device int32)."""
+    n = expert_idx.numel()
+    y = y if y is not None else torch.empty(n, pool.hidden, dtype=torch.float32, device=x.device)
+    need = qmoe_ffn_workspace_bytes(pool, n)
+    ws = ws if ws is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.expert_ffn_swiglu(ctypes.byref(pool.c()), _ptr(expert_idx, torch.int32, "expert_idx"), n,
+                                  _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"),
+                                  _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream()),
+           "expert_ffn_swiglu")
+    return y
+
+
+def moe_combine_residual_gate(y_routed, topk_w, y_shared, shared_gate, x, residual, out=None):
+    H = x.numel()
+    K = topk_w.numel()
+    out = out if out is not None else torch.empty(H, dtype=torch.float32, device=x.device)
+    _check(_lib.moe_combine_residual_gate(_ptr(y_routed, torch.float32, "y_routed"),
+                                          _ptr(topk_w, torch.float32, "topk_w"),
+                                          _ptr(y_shared, torch.float32, "y_shared"),
+                                          _ptr(shared_gate, None, "shared_gate"),
+                                          _ptr(x, torch.float32, "x"), _ptr(residual, torch.float32, "residual"),
+                                          _ptr(out, torch.float32, "out"), H, K, _stream()),
+           "moe_combine_residual_gate")
+    return out
+
+
+def moe_layer_forward(layer: Layer, x, residual=None, out=None, idx=None, w=None, ws=None):
+    """One fused launch: returns (out [H], idx int32 [K], w [K])."""
+    residual = residual if residual is not None else x
+    dev = x.device
+    out = out if out is not None else torch.empty_like(x)
+    idx = idx if idx is not None else torch.empty(layer.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(layer.top_k, dtype=torch.float32, device=dev)
+    if ws is None:
+        raise ValueError("pass a persistent workspace from alloc_workspace(layer)")
+    _check(_lib.moe_layer_forward(ctypes.byref(layer.c()), _ptr(x, torch.float32, "x"),
+                                  _ptr(residual, torch.float32, "residual"), _ptr(out, torch.float32, "out"),
+                                  _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
+                                  _ptr(ws, None, "ws"), ws.numel(), _stream()), "moe_layer_forward")
+    return out, idx, w
+
+
+def moe_layer_forward_batched(layer: Layer, x, residual=None, out=None, idx=None, w=None, ws=None):
+    """T tokens x [T][H]: returns (out [T][H], idx [T][K], w [T][K])."""
+    T = x.shape[0]
+    residual = residual if residual is not None else x
+    dev = x.device
+    out = out if out is not None else torch.empty_like(x)
+    idx = idx if idx is not None else torch.empty(T, layer.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(T, layer.top_k, dtype=torch.float32, device=dev)
+    if ws is None:
+        raise ValueError("pass a persistent workspace from alloc_workspace(layer, T)")
+    _check(_lib.moe_layer_forward_batched(ctypes.byref(layer.c()), _ptr(x, torch.float32, "x"),
+                                          _ptr(residual, torch.float32, "residual"),
+                                          _ptr(out, torch.float32, "out"), T,
+                                          _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
+                                          _ptr(ws, None, "ws"), ws.numel(), _stream()),
+           "moe_layer_forward_batched")
+    return out, idx, w
+
+
+def rmsnorm_f32(v, weight, eps=1e-6, out=None):
+    out = out if out is not None else torch.empty_like(v)
+    _check(_lib.rmsnorm_f32(_ptr(v, torch.float32, "v"), _ptr(weight, torch.float32, "w"), eps, v.numel(),
+                            _ptr(out, torch.float32, "out"), _stream()), "rmsnorm_f32")
+    return out
+
+
+def raw_lib():
+    """The ctypes handle (for tests of the C ABI itself)."""
+    return _lib

@@ -1,0 +1,256 @@
+// C ABI front end of libqmoe: validates every argument on the host, then
+// enqueues the kernels on the caller's stream.  Nothing here allocates, frees
+// or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qmoe_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QMOE_OK;
+  return fail(QMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_vec(const void* p, const char* name) {
+  if (!p) return fail(QMOE_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(QMOE_EALIGN, "%s must be 16-byte aligned", name);
+  return QMOE_OK;
+}
+
+int check_pool(const qmoe_expert_pool* p, const char* name) {
+  if (!p) return fail(QMOE_EINVAL, "%s is NULL", name);
+  if (!p->base) return fail(QMOE_EINVAL, "%s.base is NULL", name);
+  if (p->bits != 2 && p->bits != 4) return fail(QMOE_EINVAL, "%s.bits must be 2 or 4", name);
+  if (p->num_experts < 1 || p->num_experts > qmoe::kMaxExperts)
+    return fail(QMOE_ESHAPE, "%s.num_experts must be in [1, %d]", name, qmoe::kMaxExperts);
+  if (p->hidden < 64 || p->inter < 64 || p->hidden % 64 || p->inter % 64)
+    return fail(QMOE_ESHAPE, "%s: hidden and inter must be positive multiples of 64", name);
+  const int maxc = p->bits == 4 ? qmoe::kMaxCols4 : qmoe::kMaxCols2;
+  if (p->hidden > maxc || p->inter > maxc)
+    return fail(QMOE_ESHAPE, "%s: hidden and inter must be at most %d at %d bits", name, maxc,
+                p->bits);
+  const qmoe_expert_offsets o = qmoe::expert_offsets(p->hidden, p->inter, p->bits);
+  if (p->stride < o.total || p->stride % 256)
+    return fail(QMOE_EALIGN, "%s.stride must be >= %lld and a multiple of 256", name,
+                (long long)o.total);
+  if (!aligned(p->base, 256)) return fail(QMOE_EALIGN, "%s.base must be 256-byte aligned", name);
+  return QMOE_OK;
+}
+
+int check_layer(const qmoe_layer* L) {
+  if (!L) return fail(QMOE_EINVAL, "layer is NULL");
+  int rc = check_pool(&L->routed, "routed");
+  if (rc) return rc;
+  rc = check_pool(&L->shared, "shared");
+  if (rc) return rc;
+  if (L->shared.num_experts != 1) return fail(QMOE_ESHAPE, "shared.num_experts must be 1");
+  if (L->shared.hidden != L->routed.hidden || L->shared.inter != L->routed.inter ||
+      L->shared.bits != L->routed.bits)
+    return fail(QMOE_ESHAPE, "shared and routed experts must have the same shape and bits");
+  if (L->top_k < 1 || L->top_k > qmoe::kMaxTopK || L->top_k > L->routed.num_experts)
+    return fail(QMOE_ESHAPE, "top_k must be in [1, min(E, %d)]", qmoe::kMaxTopK);
+  if (L->routed.hidden > qmoe::kMaxRouterH)
+    return fail(QMOE_ESHAPE, "hidden must be at most %d", qmoe::kMaxRouterH);
+  if (!L->router || !aligned(L->router, 16)) return fail(QMOE_EALIGN, "router must be 16-byte aligned");
+  if (!L->shared_gate || !aligned(L->shared_gate, 16))
+    return fail(QMOE_EALIGN, "shared_gate must be 16-byte aligned");
+  return QMOE_OK;
+}
+
+int check_qmat(const qmoe_qmat* W, int bits) {
+  if (!W) return fail(QMOE_EINVAL, "W is NULL");
+  if (W->rows < 0 || W->cols < 0) return fail(QMOE_EINVAL, "negative matrix size");
+  if (W->cols < 64 || W->cols % 64) return fail(QMOE_ESHAPE, "cols must be a positive multiple of 64");
+  const int maxc = bits == 4 ? qmoe::kMaxCols4 : qmoe::kMaxCols2;
+  if (W->cols > maxc) return fail(QMOE_ESHAPE, "cols must be at most %d at %d bits", maxc, bits);
+  if (W->rows > 0) {
+    if (!W->codes || !W->sb) return fail(QMOE_EINVAL, "codes/sb is NULL");
+    if (!aligned(W->codes, 16)) return fail(QMOE_EALIGN, "codes must be 16-byte aligned");
+    if (!aligned(W->sb, 4)) return fail(QMOE_EALIGN, "sb must be 4-byte aligned");
+  }
+  return QMOE_OK;
+}
+
+}  // namespace
+
+namespace qmoe {
+
+qmoe_expert_offsets expert_offsets(int hidden, int inter, int bits) {
+  qmoe_expert_offsets o;
+  const int64_t gu = (int64_t)inter * hidden * bits / 8;
+  const int64_t dn = (int64_t)hidden * inter * bits / 8;
+  const int64_t gsb = (int64_t)inter * (hidden / 64) * 4;
+  const int64_t dsb = (int64_t)hidden * (inter / 64) * 4;
+  o.gate_codes = 0;
+  o.up_codes = gu;
+  o.down_codes = 2 * gu;
+  o.gate_sb = 2 * gu + dn;
+  o.up_sb = o.gate_sb + gsb;
+  o.down_sb = o.up_sb + gsb;
+  o.total = o.down_sb + dsb;
+  return o;
+}
+
+}  // namespace qmoe
+
+extern "C" {
+
+int qmoe_expert_layout(int32_t hidden, int32_t inter, int32_t bits, qmoe_expert_offsets* out) {
+  if (!out) return fail(QMOE_EINVAL, "out is NULL");
+  if (bits != 2 && bits != 4) return fail(QMOE_EINVAL, "bits must be 2 or 4");
+  if (hidden < 64 || inter < 64 || hidden % 64 || inter % 64)
+    return fail(QMOE_ESHAPE, "hidden and inter must be positive multiples of 64");
+  *out = qmoe::expert_offsets(hidden, inter, bits);
+  return QMOE_OK;
+}
+
+static int qgemv_common(const qmoe_qmat* W, const float* x, float* y, void* stream, int bits) {
+  int rc = check_qmat(W, bits);
+  if (rc) return rc;
+  if (W->rows == 0) return QMOE_OK;
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!y) return fail(QMOE_EINVAL, "y is NULL");
+  return hip_status(qmoe::launch_qgemv(bits, static_cast<const uint8_t*>(W->codes), W->sb, x, y,
+                                       W->rows, W->cols, static_cast<hipStream_t>(stream)),
+                    "qgemv launch");
+}
+
+int qgemv_w4(const qmoe_qmat* W, const float* x, float* y, void* stream) {
+  return qgemv_common(W, x, y, stream, 4);
+}
+
+int qgemv_w2(const qmoe_qmat* W, const float* x, float* y, void* stream) {
+  return qgemv_common(W, x, y, stream, 2);
+}
+
+int moe_router_topk(const uint16_t* router, const float* x, int32_t T, int32_t H, int32_t E,
+                    int32_t K, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (T < 0 || H < 0 || E < 0 || K < 0) return fail(QMOE_EINVAL, "negative size");
+  if (H < 64 || H % 64 || H > qmoe::kMaxRouterH)
+    return fail(QMOE_ESHAPE, "H must be a multiple of 64 in [64, %d]", qmoe::kMaxRouterH);
+  if (E < 1 || E > qmoe::kMaxExperts) return fail(QMOE_ESHAPE, "E must be in [1, %d]", qmoe::kMaxExperts);
+  if (K < 1 || K > E || K > qmoe::kMaxTopK) return fail(QMOE_ESHAPE, "K must be in [1, min(E, 8)]");
+  if (T == 0) return QMOE_OK;
+  if (!router || !aligned(router, 16)) return fail(QMOE_EALIGN, "router must be 16-byte aligned");
+  int rc;
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!logits || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "output pointer is NULL");
+  return hip_status(qmoe::launch_router_topk(router, x, T, H, E, K, logits, topk_idx, topk_w,
+                                             static_cast<hipStream_t>(stream)),
+                    "router launch");
+}
+
+size_t qmoe_ffn_workspace_bytes(const qmoe_expert_pool* pool, int32_t n) {
+  if (!pool || n < 0 || pool->inter < 0) return 0;
+  return (size_t)n * (size_t)pool->inter * sizeof(float);
+}
+
+int expert_ffn_swiglu(const qmoe_expert_pool* pool, const int32_t* expert_idx, int32_t n,
+                      const float* x, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_pool(pool, "pool");
+  if (rc) return rc;
+  if (n < 0) return fail(QMOE_EINVAL, "n must be >= 0");
+  if (n > 65535) return fail(QMOE_ESHAPE, "n must be at most 65535");
+  if (n == 0) return QMOE_OK;
+  if (!expert_idx) return fail(QMOE_EINVAL, "expert_idx is NULL");
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!y) return fail(QMOE_EINVAL, "y is NULL");
+  if (!ws || ws_bytes < qmoe_ffn_workspace_bytes(pool, n))
+    return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", qmoe_ffn_workspace_bytes(pool, n));
+  if (!aligned(ws, 16)) return fail(QMOE_EALIGN, "ws must be 16-byte aligned");
+  return hip_status(qmoe::launch_ffn(*pool, expert_idx, n, x, 0, y, static_cast<float*>(ws),
+                                     static_cast<hipStream_t>(stream)),
+                    "expert_ffn launch");
+}
+
+int moe_combine_residual_gate(const float* y_routed, const float* topk_w, const float* y_shared,
+                              const uint16_t* shared_gate, const float* x, const float* residual,
+                              float* out, int32_t H, int32_t K, void* stream) {
+  if (H < 0 || K < 0) return fail(QMOE_EINVAL, "negative size");
+  if (K > qmoe::kMaxTopK) return fail(QMOE_ESHAPE, "K must be at most %d", qmoe::kMaxTopK);
+  if (H == 0) return QMOE_OK;
+  if ((K > 0 && (!y_routed || !topk_w)) || !y_shared || !shared_gate || !x || !residual || !out)
+    return fail(QMOE_EINVAL, "NULL pointer");
+  return hip_status(qmoe::launch_combine(y_routed, topk_w, y_shared, shared_gate, x, residual, out,
+                                         H, K, static_cast<hipStream_t>(stream)),
+                    "combine launch");
+}
+
+size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t T) {
+  if (!L || T < 1 || T > qmoe::kMaxBatch) return 0;
+  if (T == 1) return qmoe::layer_workspace_bytes(*L);
+  return qmoe::batched_workspace_bytes(*L, T);
+}
+
+int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual, float* out,
+                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!residual || !out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  if (out == x) return fail(QMOE_EINVAL, "out must not alias x");
+  const size_t need = qmoe_workspace_bytes(L, 1);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  return hip_status(qmoe::launch_layer(*L, x, residual, out, topk_idx, topk_w, ws,
+                                       static_cast<hipStream_t>(stream)),
+                    "moe_layer_forward launch");
+}
+
+int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* residual,
+                              float* out, int32_t T, int32_t* topk_idx, float* topk_w, void* ws,
+                              size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 1 || T > qmoe::kMaxBatch) return fail(QMOE_ESHAPE, "T must be in [1, %d]", qmoe::kMaxBatch);
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!residual || !out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  if (out == x) return fail(QMOE_EINVAL, "out must not alias x");
+  const size_t need = qmoe_workspace_bytes(L, T);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  return hip_status(qmoe::launch_layer_batched(*L, x, residual, out, T, topk_idx, topk_w, ws,
+                                               static_cast<hipStream_t>(stream)),
+                    "moe_layer_forward_batched launch");
+}
+
+int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out, void* stream) {
+  if (n < 0) return fail(QMOE_EINVAL, "n must be >= 0");
+  if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");
+  if (n == 0) return QMOE_OK;
+  if (!v || !w || !out) return fail(QMOE_EINVAL, "NULL pointer");
+  return hip_status(qmoe::launch_rmsnorm(v, w, eps, n, out, static_cast<hipStream_t>(stream)),
+                    "rmsnorm launch");
+}
+
+const char* qmoe_strerror(int status) {
+  switch (status) {
+    case QMOE_OK: return "ok";
+    case QMOE_EINVAL: return "invalid argument";
+    case QMOE_ESHAPE: return "unsupported shape";
+    case QMOE_EALIGN: return "misaligned pointer or stride";
+    case QMOE_EWORKSPACE: return "workspace too small";
+    case QMOE_EHIP: return "HIP runtime error";
+    case QMOE_EUNSUPPORTED: return "not supported";
+    default: return "unknown status";
+  }
+}
+
+const char* qmoe_last_error(void) { return g_last_error; }
+
+}  // extern "C"

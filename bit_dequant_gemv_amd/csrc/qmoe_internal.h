@@ -1,0 +1,50 @@
+// Internal host-side launch interface between the C ABI (api.cpp) and the
+// kernel translation units.  Arguments arrive validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmoe.h"
+
+namespace qmoe {
+
+// largest input width kept in registers per lane group
+constexpr int kMaxCols4 = 8192;
+constexpr int kMaxCols2 = 16384;
+constexpr int kMaxRouterH = 8192;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxBatch = 256;
+
+hipError_t launch_qgemv(int bits, const uint8_t* codes, const uint32_t* sb, const float* x,
+                        float* y, int rows, int cols, hipStream_t s);
+
+hipError_t launch_ffn(const qmoe_expert_pool& pool, const int32_t* idx, int n, const float* x,
+                      int64_t x_stride, float* y, float* h_ws, hipStream_t s);
+
+hipError_t launch_router_topk(const uint16_t* router, const float* x, int T, int H, int E, int K,
+                              float* logits, int32_t* idx, float* w, hipStream_t s);
+
+hipError_t launch_combine(const float* y_routed, const float* w, const float* y_shared,
+                          const uint16_t* g, const float* x, const float* residual, float* out,
+                          int H, int K, hipStream_t s);
+
+hipError_t launch_rmsnorm(const float* v, const float* w, float eps, int n, float* out,
+                          hipStream_t s);
+
+// fused single-launch layer (layer.hip)
+size_t layer_workspace_bytes(const qmoe_layer& L);
+hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residual, float* out,
+                        int32_t* idx, float* w, void* ws, hipStream_t s);
+
+// batched decode (batched.hip)
+size_t batched_workspace_bytes(const qmoe_layer& L, int T);
+hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float* residual,
+                                float* out, int T, int32_t* idx, float* w, void* ws,
+                                hipStream_t s);
+
+// offsets of the canonical expert block
+qmoe_expert_offsets expert_offsets(int hidden, int inter, int bits);
+
+}  // namespace qmoe

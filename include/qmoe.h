@@ -1,0 +1,190 @@
+/*
+ * qmoe.h -- C ABI of libqmoe: batch-1 quantized mixture-of-experts expert forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are web pages about the Flash-MoE engine; cited by
+ * page title and section):
+ *   [PK] "flash-moe 소개", PyTorch Korea user group forum (discuss.pytorch.kr
+ *        topic 9315): sections "FMA 최적화 역양자화 커널" (affine dequant
+ *        w = nibble*scale + bias and its FMA rearrangement), "손으로 작성한 Metal
+ *        컴퓨트 셰이더" (4/2-bit dequant matrix-vector kernels, fused SwiGLU,
+ *        two-stage RMSNorm, fused MoE combine + residual + sigmoid gate),
+ *        "레이어당 파이프라인 상세 구조" (router in the second command buffer,
+ *        softmax + top-K, expert forward + combine deferred in the third) and
+ *        "Qwen3.5-397B-A17B 모델 아키텍처" (512 experts, K=4 active plus one
+ *        shared expert, hidden 4096).
+ *
+ * Conventions for every function below
+ *   - Array pointers are DEVICE pointers owned by the caller (for example torch
+ *     tensors); struct pointers (qmoe_qmat*, qmoe_layer*, ...) are HOST
+ *     pointers read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously; no call synchronises the device, allocates or
+ *     frees memory.  Scratch memory is a caller-provided workspace.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     negative qmoe_status is returned and nothing is launched.  A launch
+ *     failure returns QMOE_EHIP.  Device faults surface at the caller's next
+ *     synchronisation, as with any stream API.  qmoe_last_error() gives a
+ *     thread-local text for the last failure.
+ *   - Buffers must stay alive until the stream has passed the call.
+ *   - Expert indices read on the device outside [0, E) are not dereferenced:
+ *     the outputs that depend on them are set to NaN.
+ *
+ * Quantized matrix layout (the pages do not give one; this library's reading)
+ *   codes : row-major, cols*bits/8 bytes per row; element k of a row is the
+ *           unsigned code in bits (k*bits)%8 upward of byte (k*bits)/8
+ *           (least-significant first).  16-byte aligned.
+ *   sb    : uint32 [rows][cols/64]; bits 0-15 = bf16 scale, bits 16-31 = bf16
+ *           bias of the group of 64 input columns.  4-byte aligned.
+ *   value : W[n][k] = q[n][k] * scale[n][k/64] + bias[n][k/64]     ([PK] FMA section)
+ *
+ * Expert block (one expert, qmoe_expert_layout gives the offsets):
+ *   gate codes, up codes, down codes, gate sb, up sb, down sb, in that order;
+ *   gate and up are inter x hidden (out x in), down is hidden x inter.
+ *   hidden 4096 / inter 1024: 7,077,888 B at 4 bits (the pages' ~6.75 MB per
+ *   expert), 3,932,160 B at 2 bits.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_EINVAL = -1,      /* null pointer, bad enum value, negative size */
+  QMOE_ESHAPE = -2,      /* sizes not supported (not a multiple of 64, too large, K > E) */
+  QMOE_EALIGN = -3,      /* a pointer or stride is not aligned as documented */
+  QMOE_EWORKSPACE = -4,  /* workspace missing or smaller than qmoe_workspace_bytes() */
+  QMOE_EHIP = -5,        /* the HIP runtime reported an error */
+  QMOE_EUNSUPPORTED = -6 /* valid request this build does not implement */
+} qmoe_status;
+
+/* Byte offsets of the six tensors inside one expert block, and its size. */
+typedef struct {
+  int64_t gate_codes, up_codes, down_codes, gate_sb, up_sb, down_sb, total;
+} qmoe_expert_offsets;
+
+/* One quantized matrix (rows = outputs, cols = inputs). */
+typedef struct {
+  const void* codes;   /* device, [rows][cols*bits/8] bytes, 16-byte aligned */
+  const uint32_t* sb;  /* device, [rows][cols/64] scale|bias words */
+  int32_t rows, cols;
+} qmoe_qmat;
+
+/* Experts resident in HBM: expert e's block starts at base + e*stride. */
+typedef struct {
+  const void* base;     /* device, 256-byte aligned */
+  int64_t stride;       /* bytes between experts: >= block size, multiple of 256 */
+  int32_t num_experts;  /* E */
+  int32_t hidden;       /* H, multiple of 64 */
+  int32_t inter;        /* I, multiple of 64 */
+  int32_t bits;         /* 2 or 4 */
+} qmoe_expert_pool;
+
+/* One MoE layer: E routed experts, one shared expert, router and shared gate. */
+typedef struct {
+  qmoe_expert_pool routed;      /* E routed experts */
+  qmoe_expert_pool shared;      /* num_experts must be 1; same hidden/inter/bits */
+  const uint16_t* router;       /* device bf16 [E][H]: logits = router . x */
+  const uint16_t* shared_gate;  /* device bf16 [H]: gamma = sigmoid(shared_gate . x) */
+  int32_t top_k;                /* K, 1 <= K <= min(E, 8) */
+} qmoe_layer;
+
+/* Pure host: offsets of an expert block for (hidden, inter, bits).  No device use. */
+int qmoe_expert_layout(int32_t hidden, int32_t inter, int32_t bits, qmoe_expert_offsets* out);
+
+/*
+ * y[rows] = W x with W 4-bit ([PK] "손으로 작성한 Metal 컴퓨트 셰이더": 4-bit dequant
+ * matrix-vector product; "FMA 최적화 역양자화 커널": w = nibble*scale + bias).
+ * x: device float[cols]; y: device float[rows] (written).  cols a multiple of 64
+ * and at most 8192; rows >= 0.  fp32 accumulation.
+ */
+int qgemv_w4(const qmoe_qmat* W, const float* x, float* y, void* stream);
+
+/* As qgemv_w4 for 2-bit codes (values 0..3); cols at most 16384. */
+int qgemv_w2(const qmoe_qmat* W, const float* x, float* y, void* stream);
+
+/*
+ * Router GEMV + softmax + top-K for T tokens ([PK] "레이어당 파이프라인 상세 구조":
+ * routing in the second command buffer, then softmax + top-K; here both on the GPU).
+ *   router  : device bf16 [E][H]
+ *   x       : device float [T][H]
+ *   logits  : device float [T][E] (written; also the kernel's scratch)
+ *   topk_idx: device int32 [T][K] (written): descending logit, ties to the lower index
+ *   topk_w  : device float [T][K] (written): softmax over the K selected logits
+ * 1 <= K <= min(E, 8), H a multiple of 64 (at most 16384), E <= 4096.
+ */
+int moe_router_topk(const uint16_t* router, const float* x, int32_t T, int32_t H, int32_t E,
+                    int32_t K, float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Expert FFN with fused SwiGLU for n experts of a pool, chosen by a device index list
+ * ([PK] Metal shaders: dequant matvec + fused SwiGLU):
+ *   y[i] = D_e (silu(G_e x) * (U_e x)),  e = expert_idx[i]
+ *   expert_idx: device int32 [n]; x: device float [H]; y: device float [n][H] (written)
+ *   ws: device scratch of at least qmoe_ffn_workspace_bytes(pool, n) bytes.
+ */
+int expert_ffn_swiglu(const qmoe_expert_pool* pool, const int32_t* expert_idx, int32_t n,
+                      const float* x, float* y, void* ws, size_t ws_bytes, void* stream);
+size_t qmoe_ffn_workspace_bytes(const qmoe_expert_pool* pool, int32_t n);
+
+/*
+ * Fused combine ([PK] Metal shaders: MoE combine + residual + sigmoid gate, one kernel):
+ *   out = residual + sum_i topk_w[i] * y_routed[i] + sigmoid(shared_gate . x) * y_shared
+ *   y_routed: device float [K][H]; topk_w: device float [K]; y_shared, x, residual,
+ *   out: device float [H]; shared_gate: device bf16 [H].  out may alias residual.
+ */
+int moe_combine_residual_gate(const float* y_routed, const float* topk_w, const float* y_shared,
+                              const uint16_t* shared_gate, const float* x, const float* residual,
+                              float* out, int32_t H, int32_t K, void* stream);
+
+/*
+ * One MoE layer at batch 1 in a single kernel launch: router GEMV -> top-K ->
+ * K routed + 1 shared SwiGLU expert (expert-indexed, no host round trip) ->
+ * combine with residual and sigmoid gate.  ([PK] "레이어당 파이프라인 상세 구조":
+ * the routing, expert forward and combine the reference splits over two command
+ * buffers and a host top-K.)
+ *   x, residual: device float [H]; out: device float [H] (written; must not alias x,
+ *   may alias residual); topk_idx/topk_w: device [K] (written).
+ *   ws: device workspace of at least qmoe_workspace_bytes(L, 1) bytes, 256-byte
+ *   aligned, ZERO-FILLED before its first use; each call leaves it zero-filled
+ *   again on completion.  Calls that share a workspace must be stream-ordered.
+ */
+int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual, float* out,
+                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Batched decode of T tokens through one layer (row t equals moe_layer_forward on
+ * token t): tokens are grouped per routed expert (histogram, scan, stable scatter)
+ * so each active expert's weights are read once per batch.
+ *   x, residual, out: device float [T][H]; topk_idx/topk_w: device [T][K] (written).
+ *   ws: at least qmoe_workspace_bytes(L, T) bytes, zero-filled before first use
+ *   and left zero-filled.  1 <= T <= 256.
+ */
+int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* residual,
+                              float* out, int32_t T, int32_t* topk_idx, float* topk_w, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_layer_forward (T == 1) or moe_layer_forward_batched. */
+size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t T);
+
+/*
+ * RMSNorm ([PK] Metal shaders: two-stage RMS normalisation):
+ *   out = v / sqrt(mean(v^2) + eps) * w;  v, w, out: device float [n]; out may alias v.
+ */
+int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out, void* stream);
+
+/* Static text for a status code; thread-local detail of the last failure. */
+const char* qmoe_strerror(int status);
+const char* qmoe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/qmoe.h declares, computes the expert layout on the host, and rejects
+bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bit_dequant_gemv_amd", "libqmoe.so")
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libqmoe.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = _declared_functions()
+    assert len(names) >= 12, names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_expert_layout_matches_oracle_layout():
+    import bit_dequant_gemv_amd as q
+    for H, I, bits in [(4096, 1024, 4), (4096, 1024, 2), (128, 64, 4), (1024, 256, 2)]:
+        lay = q.qmoe_expert_layout(H, I, bits)
+        off = oracle.expert_offsets(H, I, bits)
+        for name in ("gate_codes", "up_codes", "down_codes", "gate_sb", "up_sb", "down_sb"):
+            assert lay[name] == off[name][0]
+        assert lay["total"] == off["total"]
+    assert q.qmoe_expert_layout(4096, 1024, 4)["total"] == 7_077_888
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    import bit_dequant_gemv_amd as q
+    lib = q.raw_lib()
+    # bad bits / shapes in the pure-host layout call
+    o = q.ExpertOffsets()
+    assert lib.qmoe_expert_layout(4096, 1024, 3, ctypes.byref(o)) == q.QMOE_EINVAL
+    assert lib.qmoe_expert_layout(100, 1024, 4, ctypes.byref(o)) == q.QMOE_ESHAPE
+    assert lib.qmoe_expert_layout(4096, 1024, 4, None) == q.QMOE_EINVAL
+    # qgemv: null matrix, cols not a multiple of 64, misaligned codes
+    assert lib.qgemv_w4(None, None, None, None) == q.QMOE_EINVAL
+    m = q.QMat(16, 16, 4, 100)
+    assert lib.qgemv_w4(ctypes.byref(m), 16, 16, None) == q.QMOE_ESHAPE
+    m = q.QMat(17, 16, 4, 128)
+    assert lib.qgemv_w4(ctypes.byref(m), 16, 16, None) == q.QMOE_EALIGN
+    m = q.QMat(16, 16, 4, 16384)
+    assert lib.qgemv_w4(ctypes.byref(m), 16, 16, None) == q.QMOE_ESHAPE     # > 8192 at 4 bits
+    assert "multiple of 64" in lib.qmoe_last_error().decode() or "at most" in lib.qmoe_last_error().decode()
+    # router: K > E, H not a multiple of 64
+    assert lib.moe_router_topk(16, 16, 1, 4096, 4, 5, 16, 16, 16, None) == q.QMOE_ESHAPE
+    assert lib.moe_router_topk(16, 16, 1, 100, 512, 4, 16, 16, 16, None) == q.QMOE_ESHAPE
+    # expert pool: bad stride, bad bits
+    pool = q.ExpertPoolC(256, 1000, 4, 4096, 1024, 4)
+    assert lib.expert_ffn_swiglu(ctypes.byref(pool), 16, 1, 16, 16, 16, 1 << 20, None) == q.QMOE_EALIGN
+    pool = q.ExpertPoolC(256, 7077888, 4, 4096, 1024, 3)
+    assert lib.expert_ffn_swiglu(ctypes.byref(pool), 16, 1, 16, 16, 16, 1 << 20, None) == q.QMOE_EINVAL
+    # layer: short workspace, top_k > 8
+    routed = q.ExpertPoolC(256, 7077888, 512, 4096, 1024, 4)
+    shared = q.ExpertPoolC(256, 7077888, 1, 4096, 1024, 4)
+    L = q.LayerC(routed, shared, 256, 256, 4)
+    need = lib.qmoe_workspace_bytes(ctypes.byref(L), 1)
+    assert need > 0
+    assert lib.moe_layer_forward(ctypes.byref(L), 256, 256, 512, 16, 16, 256, need - 1, None) == \
+        q.QMOE_EWORKSPACE
+    assert lib.moe_layer_forward(ctypes.byref(L), 256, 256, 256, 16, 16, 256, need, None) == \
+        q.QMOE_EINVAL   # out aliases x
+    L9 = q.LayerC(routed, shared, 256, 256, 9)
+    assert lib.moe_layer_forward(ctypes.byref(L9), 256, 256, 512, 16, 16, 256, need, None) == q.QMOE_ESHAPE
+    bad_shared = q.LayerC(routed, q.ExpertPoolC(256, 7077888, 2, 4096, 1024, 4), 256, 256, 4)
+    assert lib.moe_layer_forward(ctypes.byref(bad_shared), 256, 256, 512, 16, 16, 256, need, None) == \
+        q.QMOE_ESHAPE
+    assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 256, 512, 0, 16, 16, 256, need, None) == \
+        q.QMOE_ESHAPE
+    assert lib.rmsnorm_f32(16, 16, -1.0, 4, 16, None) == q.QMOE_EINVAL
+    assert lib.qmoe_workspace_bytes(ctypes.byref(L), 0) == 0
+    assert lib.qmoe_strerror(q.QMOE_EWORKSPACE) == b"workspace too small"
+
+
+def test_workspace_grows_with_batch():
+    import bit_dequant_gemv_amd as q
+    lib = q.raw_lib()
+    routed = q.ExpertPoolC(256, 7077888, 512, 4096, 1024, 4)
+    shared = q.ExpertPoolC(256, 7077888, 1, 4096, 1024, 4)
+    L = q.LayerC(routed, shared, 256, 256, 4)
+    a = lib.qmoe_workspace_bytes(ctypes.byref(L), 1)
+    b = lib.qmoe_workspace_bytes(ctypes.byref(L), 64)
+    assert b > a > (512 + 1) * 8
+    assert b % 256 == 0 and a % 256 == 0

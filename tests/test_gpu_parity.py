@@ -1,0 +1,387 @@
+"""Parity of the HIP path (through the C ABI) against the float64 CPU oracle.
+
+Bars: expert indices equal the oracle's top-K (decided on fp32-rounded logits,
+ties to the lower index) except exempted fp32 near-ties; floating-point outputs
+within relative L2 error 1e-3 of the oracle (the stated bar), and within 1e-4
+as a tighter fp32-accumulation check.  Inputs are seeded synthetic tensors
+drawn by ``synth`` on the device and regenerated on the host for the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from qmoe_testlib import DeviceLayer, check_topk, device_x, host_x
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3       # relative L2 bar for fp32-accumulated outputs
+TIGHT = 1e-4     # fp32 accumulation is ~1e-6 here; this catches real defects early
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def q():
+    import bit_dequant_gemv_amd as q
+    return q
+
+
+def _rel(a, b):
+    return oracle.rel_l2(np.asarray(a, dtype=np.float64), b)
+
+
+# ---------------------------------------------------------------------------
+# generators: device fill == host fill, bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,I,bits,E", [(128, 64, 4, 3), (192, 128, 2, 2), (4096, 1024, 4, 1)])
+def test_synth_device_matches_host(q, H, I, bits, E):
+    say("synth pool", H, I, bits, E)
+    pool = q.ExpertPool.allocate(E, H, I, bits)
+    synth.fill_expert_pool(pool.buf, pool.stride, E, 5, 3, 77, H, I, bits)
+    torch.cuda.synchronize()
+    for e in range(E):
+        dev = pool.expert_bytes(e).cpu().numpy()
+        host = synth.expert_block(77, 3, 5 + e, H, I, bits)
+        np.testing.assert_array_equal(dev, host)
+
+
+def test_synth_device_value_streams(q):
+    say("synth value streams")
+    n = 10007
+    t = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.fill_normal_bf16(t, 9, 123, 0.02)
+    np.testing.assert_array_equal(t.cpu().numpy().view(np.uint16),
+                                  synth.f32_to_bf16_bits(synth.normal_f32(9, 123, n, 0.02)))
+    f = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.fill_normal_f32(f, 9, 124, 1.0)
+    np.testing.assert_array_equal(f.cpu().numpy(), synth.normal_f32(9, 124, n, 1.0))
+    synth.fill_uniform_f32(f, 9, 125, 0.9, 1.1)
+    np.testing.assert_array_equal(f.cpu().numpy(), synth.uniform_f32(9, 125, n, 0.9, 1.1))
+    b = torch.empty(4 * 1001, dtype=torch.uint8, device="cuda")
+    synth.fill_bytes(b[:4003], 9, 126)
+    np.testing.assert_array_equal(b[:4003].cpu().numpy(), synth.stream_bytes(9, 126, 4003))
+
+
+# ---------------------------------------------------------------------------
+# quantized GEMV
+# ---------------------------------------------------------------------------
+
+GEMV_SHAPES = [(1, 64), (63, 128), (64, 4096), (1000, 1024), (4096, 1024), (1024, 4096),
+               (7, 8192), (129, 192), (33, 320)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("rows,cols", GEMV_SHAPES)
+def test_qgemv_parity(q, bits, rows, cols):
+    say("qgemv", bits, rows, cols)
+    seed = 1000 + rows * 7 + cols
+    codes, sb = synth.matrix(seed, 0, 0, 0, rows, cols, bits)
+    x = synth.normal_f32(seed, 99, cols, 1.0)
+    fn = q.qgemv_w4 if bits == 4 else q.qgemv_w2
+    y = fn(torch.from_numpy(codes).cuda(), torch.from_numpy(sb.view(np.int32)).cuda(),
+           torch.from_numpy(x).cuda())
+    ref = oracle.qgemv(codes, sb, x, bits)
+    r = _rel(y.cpu().numpy(), ref)
+    say("  rel_l2", r)
+    assert r <= TOL and r <= TIGHT
+
+
+def test_qgemv_empty_and_unit_vectors(q):
+    say("qgemv empty / unit")
+    codes, sb = synth.matrix(5, 0, 0, 0, 0, 128, 4)
+    y = torch.full((1,), 7.0, device="cuda")
+    q.qgemv_w4(torch.zeros(0, 64, dtype=torch.uint8, device="cuda"),
+               torch.zeros(0, 2, dtype=torch.int32, device="cuda"),
+               torch.zeros(128, device="cuda"), y=y)
+    assert y.item() == 7.0     # nothing written for 0 rows
+    codes, sb = synth.matrix(6, 0, 0, 0, 37, 256, 4)
+    dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(sb.view(np.int32)).cuda()
+    W = oracle.dequant(codes, sb, 256, 4)
+    for k in (0, 1, 31, 32, 63, 64, 255):
+        x = np.zeros(256, np.float32)
+        x[k] = 1.0
+        y = q.qgemv_w4(dc, ds, torch.from_numpy(x).cuda()).cpu().numpy()
+        np.testing.assert_allclose(y, W[:, k], rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# expert FFN
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,I,bits,E,idx", [(256, 128, 4, 4, [2, 0, 2]), (256, 128, 2, 3, [1]),
+                                            (4096, 1024, 4, 2, [1]), (4096, 1024, 4, 2, [0, 1, 1, 0, 1]),
+                                            (4096, 1024, 2, 2, [1, 0]), (1024, 320, 4, 3, [2, 1])])
+def test_expert_ffn_parity(q, H, I, bits, E, idx):
+    say("expert_ffn", H, I, bits, E, idx)
+    seed = 1000
+    pool = q.ExpertPool.allocate(E, H, I, bits)
+    synth.fill_expert_pool(pool.buf, pool.stride, E, 0, 0, seed, H, I, bits)
+    x = host_x(seed, 0, H)
+    y = q.expert_ffn_swiglu(pool, torch.tensor(idx, dtype=torch.int32, device="cuda"),
+                            torch.from_numpy(x).cuda()).cpu().numpy()
+    for i, e in enumerate(idx):
+        ref = oracle.expert_ffn(synth.expert_block(seed, 0, e, H, I, bits), x, H, I, bits)
+        r = _rel(y[i], ref)
+        say("  slot", i, "expert", e, "rel_l2", r)
+        assert r <= TOL and r <= TIGHT
+
+
+def test_expert_ffn_bad_index_gives_nan(q):
+    say("expert_ffn bad index")
+    pool = q.ExpertPool.allocate(2, 256, 128, 4)
+    synth.fill_expert_pool(pool.buf, pool.stride, 2, 0, 0, 3, 256, 128, 4)
+    y = q.expert_ffn_swiglu(pool, torch.tensor([1, 7, -1], dtype=torch.int32, device="cuda"),
+                            torch.from_numpy(host_x(3, 0, 256)).cuda()).cpu().numpy()
+    assert np.isfinite(y[0]).all() and np.isnan(y[1]).all() and np.isnan(y[2]).all()
+
+
+# ---------------------------------------------------------------------------
+# router + top-K, combine, RMSNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,H,K,T", [(512, 4096, 4, 5), (64, 1024, 8, 3), (10, 256, 3, 2), (4096, 512, 2, 1)])
+def test_router_topk_parity(q, E, H, K, T):
+    say("router_topk", E, H, K, T)
+    seed = 2000 + E
+    R = synth.router(seed, 0, E, H)
+    X = np.stack([host_x(seed, t, H) for t in range(T)])
+    idx, w, logits = q.moe_router_topk(torch.from_numpy(R.view(np.int16)).cuda(),
+                                       torch.from_numpy(X).cuda(), K)
+    idx, w, logits = idx.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy()
+    for t in range(T):
+        ref_l = oracle.router_logits(R, X[t])
+        assert _rel(logits[t], ref_l) <= TIGHT
+        tau = oracle.topk_tolerance(R, X[t])
+        ex = check_topk(idx[t], ref_l, tau, K)
+        sel = ref_l[idx[t]]
+        ref_w = np.exp(sel - sel.max())
+        ref_w /= ref_w.sum()
+        assert _rel(w[t], ref_w) <= TIGHT
+        say("  token", t, "near-tie exemptions", ex)
+
+
+def test_router_exact_ties_go_to_lower_index(q):
+    say("router ties")
+    E, H = 512, 4096
+    R = synth.router(31, 0, E, H).copy()
+    X = host_x(31, 0, H)
+    # a dominant row (parallel to x) copied to three experts: identical fp32 logits
+    R[7] = synth.f32_to_bf16_bits((0.02 * X).astype(np.float32))
+    R[300] = R[7]
+    R[450] = R[7]
+    idx, w, _ = q.moe_router_topk(torch.from_numpy(R.view(np.int16)).cuda(),
+                                  torch.from_numpy(X).cuda(), 4)
+    got = idx.cpu().numpy()[0].tolist()
+    assert got[:3] == [7, 300, 450], got
+    np.testing.assert_allclose(w.cpu().numpy()[0][:3], w.cpu().numpy()[0][0], rtol=0)
+
+
+def test_combine_parity(q):
+    say("combine")
+    H, K = 4096, 4
+    rng = np.random.default_rng(5)
+    yr = rng.standard_normal((K, H)).astype(np.float32)
+    w = rng.dirichlet(np.ones(K)).astype(np.float32)
+    ys = rng.standard_normal(H).astype(np.float32)
+    g = synth.shared_gate(5, 0, H)
+    x = host_x(5, 0, H)
+    r = rng.standard_normal(H).astype(np.float32)
+    c = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = q.moe_combine_residual_gate(c(yr), c(w), c(ys), c(g.view(np.int16)), c(x), c(r)).cpu().numpy()
+    ref = oracle.combine_residual_gate(yr, w, ys, g, x, r)
+    assert _rel(out, ref) <= TIGHT
+    # out aliasing the residual
+    rr = c(r)
+    q.moe_combine_residual_gate(c(yr), c(w), c(ys), c(g.view(np.int16)), c(x), rr, out=rr)
+    assert _rel(rr.cpu().numpy(), ref) <= TIGHT
+
+
+@pytest.mark.parametrize("n", [1, 64, 4096, 5000])
+def test_rmsnorm_parity(q, n):
+    say("rmsnorm", n)
+    v = synth.normal_f32(8, 1, n, 1.0)
+    w = synth.uniform_f32(8, 2, n, 0.9, 1.1)
+    out = q.rmsnorm_f32(torch.from_numpy(v).cuda(), torch.from_numpy(w).cuda(), 1e-6).cpu().numpy()
+    assert _rel(out, oracle.rmsnorm(v, w, 1e-6)) <= TIGHT
+    vv = torch.from_numpy(v).cuda()
+    q.rmsnorm_f32(vv, torch.from_numpy(w).cuda(), 1e-6, out=vv)
+    assert _rel(vv.cpu().numpy(), oracle.rmsnorm(v, w, 1e-6)) <= TIGHT
+
+
+# ---------------------------------------------------------------------------
+# one MoE layer
+# ---------------------------------------------------------------------------
+
+def _status(ws):
+    return int(ws[4:8].view(torch.int32).item())
+
+
+def _epoch(ws):
+    return int(ws[0:4].view(torch.int32).item())
+
+
+def _check_layer_token(D, x, out, idx, w, residual=None):
+    residual = x if residual is None else residual
+    R = D.host_router()
+    logits = oracle.router_logits(R, x)
+    tau = oracle.topk_tolerance(R, x)
+    ex = check_topk(idx, logits, tau, D.K)
+    ref = oracle.moe_layer(D.host_expert, D.host_shared(), R, D.host_gate(), x, residual,
+                           D.H, D.I, D.bits, D.K, force_idx=idx if ex else None)
+    r = _rel(out, ref)
+    say("  idx", list(idx), "near-ties", ex, "rel_l2", r)
+    assert r <= TOL and r <= TIGHT
+    sel = logits[np.asarray(idx)]
+    ref_w = np.exp(sel - sel.max())
+    assert _rel(w, ref_w / ref_w.sum()) <= TIGHT
+    return ex
+
+
+LAYER_CASES = [  # (E, H, I, bits, K)  -- fused shapes, plus shapes served by the fallback chain
+    (64, 1024, 256, 4, 4), (64, 1024, 256, 2, 4), (100, 2048, 512, 4, 3), (33, 1024, 512, 4, 1),
+    (16, 192, 128, 4, 2), (512, 4096, 1024, 4, 8),
+]
+
+
+@pytest.mark.parametrize("E,H,I,bits,K", LAYER_CASES)
+def test_layer_parity(q, E, H, I, bits, K):
+    say("layer", E, H, I, bits, K)
+    D = DeviceLayer(3000 + E, 0, E, H, I, bits, K)
+    ws = q.alloc_workspace(D.L)
+    for tok in range(2):
+        x = host_x(D.seed, tok, H)
+        out, idx, w = q.moe_layer_forward(D.L, torch.from_numpy(x).cuda(), ws=ws)
+        torch.cuda.synchronize()
+        assert _status(ws) == 0
+        _check_layer_token(D, x, out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy())
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_layer_full_config(q, bits):
+    """The workload layer: 512 experts (4096 x 1024, group 64), top-4, shared expert."""
+    say("layer full config bits", bits)
+    seed = 1001 if bits == 4 else 1002
+    D = DeviceLayer(seed, 0, 512, 4096, 1024, bits, 4)
+    ws = q.alloc_workspace(D.L)
+    resid = host_x(seed, 1000, 4096)
+    for tok in range(3):
+        x = host_x(seed, tok, 4096)
+        # residual distinct from x on one token (the stack passes the pre-norm h)
+        r = resid if tok == 2 else x
+        out, idx, w = q.moe_layer_forward(D.L, torch.from_numpy(x).cuda(), torch.from_numpy(r).cuda(),
+                                          ws=ws)
+        torch.cuda.synchronize()
+        assert _status(ws) == 0
+        _check_layer_token(D, x, out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), residual=r)
+
+
+def test_layer_fused_equals_unfused_chain_and_is_deterministic(q):
+    say("fused vs unfused chain")
+    D = DeviceLayer(1001, 0, 512, 4096, 1024, 4, 4)
+    ws = q.alloc_workspace(D.L)
+    xs = device_x(1001, [11, 12, 13], 4096)
+    for t in range(3):
+        x = xs[t].contiguous()
+        e0 = _epoch(ws)
+        out1, idx1, w1 = q.moe_layer_forward(D.L, x, ws=ws)
+        out2, idx2, w2 = q.moe_layer_forward(D.L, x, ws=ws)
+        torch.cuda.synchronize()
+        assert _epoch(ws) == e0 + 2 and _status(ws) == 0
+        assert torch.equal(out1, out2) and torch.equal(idx1, idx2) and torch.equal(w1, w2)
+        # the same layer through the stand-alone entry points
+        idx, w, _ = q.moe_router_topk(D.router, x, 4)
+        assert torch.equal(idx[0], idx1)
+        yr = q.expert_ffn_swiglu(D.routed, idx[0].contiguous(), x)
+        ys = q.expert_ffn_swiglu(D.shared, torch.zeros(1, dtype=torch.int32, device="cuda"), x)
+        out3 = q.moe_combine_residual_gate(yr, w[0].contiguous(), ys[0].contiguous(), D.gate, x, x)
+        r = _rel(out1.cpu().numpy(), out3.cpu().numpy().astype(np.float64))
+        say("  fused vs chain rel_l2", r)
+        assert r <= 1e-5
+
+
+def test_layer_output_may_alias_residual(q):
+    say("layer out aliases residual")
+    D = DeviceLayer(4001, 0, 64, 1024, 256, 4, 4)
+    ws = q.alloc_workspace(D.L)
+    x = host_x(D.seed, 0, 1024)
+    r = host_x(D.seed, 5, 1024)
+    rr = torch.from_numpy(r).cuda()
+    out, idx, w = q.moe_layer_forward(D.L, torch.from_numpy(x).cuda(), rr, out=rr, ws=ws)
+    torch.cuda.synchronize()
+    _check_layer_token(D, x, rr.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), residual=r)
+
+
+# ---------------------------------------------------------------------------
+# batched decode (tokens grouped per expert)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,H,I,bits,K,T", [(64, 1024, 256, 4, 4, 16), (512, 4096, 1024, 4, 4, 64),
+                                            (512, 4096, 1024, 2, 4, 8), (8, 256, 128, 4, 8, 5)])
+def test_batched_parity(q, E, H, I, bits, K, T):
+    say("batched", E, H, I, bits, K, T)
+    D = DeviceLayer(1004 if E == 512 else 5000 + E, 0, E, H, I, bits, K)
+    X = device_x(D.seed, range(T), H)
+    ws = q.alloc_workspace(D.L, T)
+    out, idx, w = q.moe_layer_forward_batched(D.L, X, ws=ws)
+    torch.cuda.synchronize()
+    out, idx, w = out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    Xh = X.cpu().numpy()
+    # every row: routing against the oracle's logits
+    R = D.host_router()
+    for t in range(T):
+        check_topk(idx[t], oracle.router_logits(R, Xh[t]), oracle.topk_tolerance(R, Xh[t]), K)
+    # sampled rows against the full oracle layer
+    for t in sorted({0, T // 2, T - 1}):
+        say("  token", t)
+        _check_layer_token(D, Xh[t], out[t], idx[t], w[t])
+    # batch invariance: each row equals the single-token fused layer
+    if E <= 512:
+        ws1 = q.alloc_workspace(D.L)
+        for t in range(0, T, max(1, T // 8)):
+            o1, i1, _ = q.moe_layer_forward(D.L, X[t].contiguous(), ws=ws1)
+            if (i1.cpu().numpy() == idx[t]).all():
+                assert _rel(out[t], o1.cpu().numpy().astype(np.float64)) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# layer stack (RMSNorm before every layer, residual = pre-norm h)
+# ---------------------------------------------------------------------------
+
+def test_stack_parity(q):
+    """A 3-layer stack at the workload's per-layer shape, 2 tokens, end to end."""
+    L_, E, H, I, K = 3, 512, 4096, 1024, 4
+    seed = 1003
+    say("stack", L_, "layers")
+    layers = [DeviceLayer(seed, l, E, H, I, 4, K) for l in range(L_)]
+    norm_w = [synth.norm_weight(seed, l, H) for l in range(L_)]
+    dnorm = [torch.from_numpy(w).cuda() for w in norm_w]
+    ws = [q.alloc_workspace(D.L) for D in layers]
+    for tok in range(2):
+        h0 = host_x(seed, tok, H)
+        h = torch.from_numpy(h0).cuda()
+        gpu_idx = []
+        for l, D in enumerate(layers):
+            x = q.rmsnorm_f32(h, dnorm[l], 1e-6)
+            out, idx, _ = q.moe_layer_forward(D.L, x, h, ws=ws[l])
+            gpu_idx.append(idx.cpu().numpy())
+            h = out
+        torch.cuda.synchronize()
+        # oracle end to end; a near-tie is resolved the way the GPU did after checking validity
+        hr = h0.astype(np.float64)
+        for l, D in enumerate(layers):
+            xr = oracle.rmsnorm(hr, norm_w[l], 1e-6)
+            R = D.host_router()
+            ex = check_topk(gpu_idx[l], oracle.router_logits(R, xr), oracle.topk_tolerance(R, xr), K)
+            hr = oracle.moe_layer(D.host_expert, D.host_shared(), R, D.host_gate(), xr, hr, H, I, 4, K,
+                                  force_idx=gpu_idx[l] if ex else None)
+        r = _rel(h.cpu().numpy(), hr)
+        say("  token", tok, "stack rel_l2", r)
+        assert r <= TOL and r <= TIGHT
