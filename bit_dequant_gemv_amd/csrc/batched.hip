@@ -166,10 +166,17 @@ __global__ __launch_bounds__(kBB) void k_bgateup(PoolArgsB P, GroupTables G,
   const int r1 = min(P.I, r0 + rows_per_block);
   const int p0 = G.group_off[gi], p1 = G.group_off[gi + 1];
   RowDot<BITS, LG, CPL> rd;
+  extern __shared__ uint32_t smem[];
+  uint32_t* planes = smem;
+  float* scl = reinterpret_cast<float*>(smem + C * QTraits<BITS>::PW);
+  float* xsum = scl + C;
   for (int pi = p0; pi < p1; ++pi) {
     const int p = G.pair_list[pi];
     const int t = token_of(p, P.T, P.K);
-    rd.load_x(x + (int64_t)t * P.H, C, gl);
+    __syncthreads();  // the previous token's planes are no longer read
+    prep_x_coop<BITS>(x + (int64_t)t * P.H, P.H, planes, scl, xsum, threadIdx.x, blockDim.x);
+    __syncthreads();
+    rd.load_prepped(planes, scl, xsum, C, gl);
     for (int j0 = r0 + wv * RPW; j0 < r1; j0 += (kBB / 64) * RPW) {
       const int j = j0 + sub;
       const bool ok = eok && j < r1;
@@ -207,9 +214,16 @@ __global__ __launch_bounds__(kBB) void k_bdown(PoolArgsB P, GroupTables G,
   const int r1 = min(P.H, r0 + rows_per_block);
   const int p0 = G.group_off[gi], p1 = G.group_off[gi + 1];
   RowDot<BITS, LG, CPL> rd;
+  extern __shared__ uint32_t smem[];
+  uint32_t* planes = smem;
+  float* scl = reinterpret_cast<float*>(smem + C * QTraits<BITS>::PW);
+  float* xsum = scl + C;
   for (int pi = p0; pi < p1; ++pi) {
     const int p = G.pair_list[pi];
-    rd.load_x(h + (int64_t)p * P.I, C, gl);
+    __syncthreads();
+    prep_x_coop<BITS>(h + (int64_t)p * P.I, P.I, planes, scl, xsum, threadIdx.x, blockDim.x);
+    __syncthreads();
+    rd.load_prepped(planes, scl, xsum, C, gl);
     for (int n0 = r0 + wv * RPW; n0 < r1; n0 += (kBB / 64) * RPW) {
       const int n = n0 + sub;
       const bool ok = eok && n < r1;
@@ -257,8 +271,9 @@ void run_bgateup(const PoolArgsB& P, const GroupTables& G, int ngroups_max, cons
                  float* h, hipStream_t s) {
   constexpr int RPW = 64 / LG;
   const int rpb = (kBB / 64) * RPW * 4;
+  const size_t lds = (size_t)(P.H / QTraits<BITS>::EPC) * (QTraits<BITS>::PW + 2) * 4;
   hipLaunchKernelGGL((k_bgateup<BITS, LG, CPL>), dim3(ceil_div(P.I, rpb), ngroups_max), dim3(kBB),
-                     0, s, P, G, x, h, rpb);
+                     lds, s, P, G, x, h, rpb);
 }
 
 template <int BITS, int LG, int CPL>
@@ -266,7 +281,8 @@ void run_bdown(const PoolArgsB& P, const GroupTables& G, int ngroups_max, const 
                hipStream_t s) {
   constexpr int RPW = 64 / LG;
   const int rpb = (kBB / 64) * RPW * 4;
-  hipLaunchKernelGGL((k_bdown<BITS, LG, CPL>), dim3(ceil_div(P.H, rpb), ngroups_max), dim3(kBB), 0,
+  const size_t lds = (size_t)(P.I / QTraits<BITS>::EPC) * (QTraits<BITS>::PW + 2) * 4;
+  hipLaunchKernelGGL((k_bdown<BITS, LG, CPL>), dim3(ceil_div(P.H, rpb), ngroups_max), dim3(kBB), lds,
                      s, P, G, h, y, rpb);
 }
 

@@ -21,6 +21,26 @@ struct RowsPerPass {
   static constexpr int R = CPL >= 4 ? 1 : (CPL == 2 ? 2 : 4);
 };
 
+// x planes of the whole input prepared once per workgroup in dynamic LDS, then
+// each lane takes its chunks' planes.  LDS: C*PW words of planes, C scales, C sums.
+template <int BITS, int LG, int CPL>
+__device__ __forceinline__ void load_x_shared(RowDot<BITS, LG, CPL>& rd, const float* x, int n, int C,
+                                              int gl) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* planes = smem;
+  float* scl = reinterpret_cast<float*>(smem + C * QTraits<BITS>::PW);
+  float* xsum = scl + C;
+  prep_x_coop<BITS>(x, n, planes, scl, xsum, threadIdx.x, blockDim.x);
+  __syncthreads();
+  rd.load_prepped(planes, scl, xsum, C, gl);
+}
+
+template <int BITS>
+inline size_t prep_lds_bytes(int n) {
+  const int C = n / QTraits<BITS>::EPC;
+  return (size_t)C * (QTraits<BITS>::PW + 2) * 4;
+}
+
 // ---------------------------------------------------------------------------
 // y = W x
 // ---------------------------------------------------------------------------
@@ -36,7 +56,7 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ co
   const int lane = threadIdx.x & 63;
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
-  rd.load_x(x, C, gl);
+  load_x_shared<BITS, LG, CPL>(rd, x, cols, C, gl);
   const int64_t nw = (int64_t)gridDim.x * (kBlock / 64);
   for (int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
        base < rows; base += nw * RPW * R) {
@@ -69,8 +89,8 @@ hipError_t run_qgemv(const uint8_t* codes, const uint32_t* sb, const float* x, f
   constexpr int R = RowsPerPass<CPL>::R;
   const int64_t waves = (rows + (64 / LG) * R - 1) / ((64 / LG) * R);
   const int blocks = (int)(waves < 4 * 8192 ? ceil_div(waves, 4) : 8192);
-  hipLaunchKernelGGL((k_qgemv<BITS, LG, CPL, R>), dim3(blocks), dim3(kBlock), 0, s, codes, sb, x,
-                     y, rows, cols);
+  hipLaunchKernelGGL((k_qgemv<BITS, LG, CPL, R>), dim3(blocks), dim3(kBlock),
+                     prep_lds_bytes<BITS>(cols), s, codes, sb, x, y, rows, cols);
   return hipGetLastError();
 }
 
@@ -136,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void k_ffn_gateup(PoolArgs P, const int32_t
   const int lane = threadIdx.x & 63;
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
-  rd.load_x(x + slot * x_stride, C, gl);
+  load_x_shared<BITS, LG, CPL>(rd, x + slot * x_stride, P.H, C, gl);
   const int nw = gridDim.x * (kBlock / 64);
   for (int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R; base < P.I;
        base += nw * RPW * R) {
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void k_ffn_down(PoolArgs P, const int32_t* 
   const int lane = threadIdx.x & 63;
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
-  rd.load_x(h + (int64_t)slot * P.I, C, gl);
+  load_x_shared<BITS, LG, CPL>(rd, h + (int64_t)slot * P.I, P.I, C, gl);
   const int nw = gridDim.x * (kBlock / 64);
   for (int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R; base < P.H;
        base += nw * RPW * R) {
@@ -219,7 +239,7 @@ hipError_t run_gateup(const PoolArgs& P, const int32_t* idx, int n, const float*
   constexpr int R = RowsPerPass<CPL>::R > 1 ? RowsPerPass<CPL>::R / 2 : 1;
   const int waves = ceil_div(P.I, (64 / LG) * R);
   hipLaunchKernelGGL((k_ffn_gateup<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock),
-                     0, s, P, idx, x, x_stride, h);
+                     prep_lds_bytes<BITS>(P.H), s, P, idx, x, x_stride, h);
   return hipGetLastError();
 }
 
@@ -228,8 +248,8 @@ hipError_t run_down(const PoolArgs& P, const int32_t* idx, int n, const float* h
                     hipStream_t s) {
   constexpr int R = RowsPerPass<CPL>::R;
   const int waves = ceil_div(P.H, (64 / LG) * R);
-  hipLaunchKernelGGL((k_ffn_down<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock), 0,
-                     s, P, idx, h, y);
+  hipLaunchKernelGGL((k_ffn_down<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock),
+                     prep_lds_bytes<BITS>(P.I), s, P, idx, h, y);
   return hipGetLastError();
 }
 

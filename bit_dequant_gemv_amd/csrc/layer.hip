@@ -4,29 +4,41 @@
 // 구조", runs this path as: router GEMV inside a second command buffer, a device
 // to host copy, softmax + top-K on the CPU, then a third command buffer with the
 // expert forward, combine and norm.  Here it is one launch with no host round
-// trip: every workgroup (all co-resident) computes the routing itself from the
-// logits, and the experts are addressed by index in the resident pool.
+// trip: every workgroup (all co-resident, one per CU) computes the routing itself
+// from the logits, and the experts are addressed by index in the resident pool.
 //
-// Data flow inside the launch (NB workgroups of 8 waves; "rank" numbers waves so
-// that consecutive ranks sit in different workgroups):
-//   A  ranks 0..E      : router rows (rank E = shared-expert gate vector g)
-//      next I/RPWH ranks: shared-expert gate/up rows + SwiGLU -> hs[I]
-//   B  each workgroup   : top-K of the E logits (redundantly, ties to the lower
-//                         index), gamma = sigmoid(g.x)
-//      all ranks       : routed gate/up rows + SwiGLU -> hr[K][I]
-//   C  workgroup b owns output rows [b*RB, b*RB+RB): down rows of the shared and
-//      the K routed experts, then out = residual + sum_k w_k y_k + gamma y_s.
-// Values that cross workgroups (logits, hs, hr) are stored as 64-bit words
-// (epoch << 32 | value bits) with agent-scope atomic stores; consumers poll the
-// words until they carry this call's epoch, so no grid barrier is needed and the
-// words never need resetting.  The epoch lives in the workspace: every wave
-// reads it at start and workgroup 0 advances it once it has consumed the
-// outputs of every wave (the grid is sized so that every wave owns at least one
-// phase-A or phase-B row, and a wave can only tag an output after reading the
-// epoch).  The down-projection codes of phase C are fetched into
-// registers before their input exists, so their HBM latency overlaps phase B.
-// Every wait is bounded; on time-out a status bit is set and the call's output
-// is undefined (it never hangs).
+// NB = H/16 workgroups of 8 waves; workgroup b owns output rows [16b, 16b+16).
+// "rank" = wave * NB + workgroup numbers the waves so that consecutive ranks sit
+// in different workgroups.  Schedule of a workgroup:
+//   1. issue loads: its router rows (4 waves per row), one shared-expert gate/up
+//      row pair per rank below I/RPWH, and (by LDS DMA) its shared-expert down rows;
+//   2. router dots -> logits (tagged stores);
+//   3. x as fixed-point planes in LDS (once per workgroup);
+//   4. shared gate/up + SwiGLU -> hs (tagged);
+//   5. wait for the E logits; top-K by ranking 64-bit keys (ties to the lower
+//      index); renormalised softmax of the K selected logits;
+//   6. issue loads: the routed down rows of its output rows (LDS DMA), the
+//      shared-gate vector g, and two routed gate/up row pairs per wave;
+//   7. routed gate/up dots + SwiGLU -> hr (tagged);
+//   8. wait for every workgroup's completion flag; read hr and hs; gamma =
+//      sigmoid(g . x); shared and routed down rows; out = residual +
+//      sum_k w_k y_k + gamma y_shared.
+// (Anything waited for after step 6's loads waits for them too: vector memory
+// results return in order.  So nothing between steps 6 and 7 waits on memory.)
+// Values that cross workgroups (logits, hs, hr) are 64-bit words (epoch << 32 |
+// value bits) written with agent-scope atomic stores (write-through to the
+// device coherence point), so they never need resetting.  The logits are polled
+// word by word.  The h values are read by every workgroup, so polling them would
+// put ~10 MB of coherent reads on a few hundred lines; instead each workgroup,
+// once all its stores are acknowledged, sets one tagged completion flag, and
+// consumers poll the 256 flags and then read h with ordinary cacheable loads
+// (one fetch per XCD's L2).  A stale cached line shows an old epoch and is
+// re-read coherently; the h buffers rotate over 4 slots so that is rare.  The
+// epoch lives in the workspace: thread 0 of every workgroup reads it before the
+// workgroup's first barrier, every flag is tagged after that barrier, and
+// workgroup 0 advances the epoch once it has seen every flag.  Every wait is
+// bounded; on time-out a status bit is set and the output is undefined (it never
+// hangs).
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -36,11 +48,11 @@ namespace {
 
 constexpr int kLB = 512;         // threads per workgroup
 constexpr int kLW = kLB / 64;    // waves per workgroup
-constexpr int kFusedMaxI = 1024;
+constexpr int kRB = 16;          // output rows per workgroup
 constexpr int kFusedMaxK = 4;
 constexpr int kFusedMaxE = 2048;
-constexpr int kMaxRoutedItems = 4;  // phase-C routed down items per wave
 constexpr uint32_t kSpinLimit = 1u << 18;
+constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see step 8
 
 // control words at the start of the workspace
 enum { CTRL_EPOCH = 0, CTRL_STATUS = 1, CTRL_ZERO = 8 };  // CTRL_ZERO is never written
@@ -58,10 +70,11 @@ struct LayerArgs {
   int32_t* idx_out;
   float* w_out;
   uint32_t* ctrl;
-  uint64_t* logits;  // [E+1]
-  uint64_t* hs;      // [I]
-  uint64_t* hr;      // [K][I]
-  int E, K, H, I, RB;
+  uint64_t* logits;  // [E]
+  uint64_t* flags;   // [NB]: workgroup b has stored (and seen acknowledged) all its h values
+  uint64_t* hs;      // [kSlotsH][I]
+  uint64_t* hr;      // [kSlotsH][K][I]
+  int E, K;
 };
 
 __device__ __forceinline__ void tag_put(uint64_t* p, float v, uint32_t tag) {
@@ -77,34 +90,39 @@ __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Copy n tagged values into LDS (every thread takes i = tid + j*kLB), waiting
-// until each carries `tag`.  Returns false on time-out.
+// Read n tagged values after their producers have all signalled completion: an
+// ordinary (L2-cacheable) load, so the 32 workgroups of an XCD share one fetch
+// from memory; a word still carrying an old tag comes from a stale cached line
+// (the buffer slot was last used several calls ago) and is re-read coherently.
 template <int PER>
-__device__ bool poll_to_lds(uint64_t* src, int n, uint32_t tag, float* dst) {
-  uint32_t pending = 0;
+__device__ void read_done_to_lds(const uint64_t* src, int n, uint32_t tag, float* dst) {
+  uint64_t v[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((int)threadIdx.x + j * kLB < n) pending |= 1u << j;
-  for (uint32_t spins = 0; pending; ++spins) {
-    uint64_t v[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = (pending >> j) & 1u ? tag_get(src + threadIdx.x + j * kLB) : 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (((pending >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
-        dst[threadIdx.x + j * kLB] = __uint_as_float((uint32_t)v[j]);
-        pending &= ~(1u << j);
-      }
-    }
-    if (!pending) break;
-    if (spins > kSpinLimit) return false;
-    __builtin_amdgcn_s_sleep(1);
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * kLB;
+    v[j] = i < n ? src[i] : 0;
   }
-  return true;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * kLB;
+    if (i < n) {
+      uint64_t w = v[j];
+      if ((uint32_t)(w >> 32) != tag) w = tag_get(const_cast<uint64_t*>(src) + i);
+      dst[i] = __uint_as_float((uint32_t)w);
+    }
+  }
 }
 
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return bi < 0 || av > bv || (av == bv && ai < bi);
+// 64-bit selection key: larger key = larger value, ties to the lower index.
+// Zero is below every key of a finite value.
+__device__ __forceinline__ uint64_t sort_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
 __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) {
@@ -118,290 +136,390 @@ __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) 
   return a0 + a1;
 }
 
-template <int BITS, int LGH, int CPLH, int LGI, int CPLR>
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+template <typename T>
+__device__ __forceinline__ lds_void_ptr lds_ptr(T* p) {
+  return (lds_void_ptr)(p);
+}
+
+// LDS DMA (global_load_lds): lane l's 16 (or 4) bytes land at lds + 16*l (4*l).
+// Kept in plain device functions: calling the builtin directly inside the kernel
+// template makes the host-side kernel handle go missing.
+__device__ __forceinline__ void dma16(const void* g, lds_void_ptr lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, lds_void_ptr lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+template <int BITS, int H, int I>
 __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
-  constexpr int RPWH = 64 / LGH;  // gate/up rows per wave pass
-  constexpr int RPWI = 64 / LGI;  // down rows per wave pass
-  constexpr int PER_L = (kFusedMaxE + 1 + kLB - 1) / kLB;
+  // ---- compile-time geometry
+  constexpr int CH = H * BITS / 128;            // 16-byte chunks per gate/up row
+  constexpr int LGH = CH >= 64 ? 64 : CH;       // lanes per gate/up row
+  constexpr int CPLH = CH / LGH;                // chunks per lane
+  constexpr int RPWH = 64 / LGH;                // gate/up rows per wave pass
+  constexpr int GH = H / kGroup;
+  constexpr int64_t RBH = (int64_t)H * BITS / 8;
+  constexpr int CI = I * BITS / 128;            // 16-byte chunks per down row
+  constexpr int LGI = CI;                       // one chunk per lane
+  static_assert(CI <= 64, "down rows must fit one chunk per lane");
+  constexpr int RPWI = 64 / LGI;                // down rows per wave pass
+  constexpr int GI = I / kGroup;
+  constexpr int64_t RBI = (int64_t)I * BITS / 8;
+  constexpr int DITEMS = (kRB + RPWI - 1) / RPWI;  // down items per expert per workgroup
+  static_assert(DITEMS <= kLW, "one shared down item per wave");
+  constexpr int MAXR = (kFusedMaxK * DITEMS + kLW - 1) / kLW;  // routed down items per wave
+  constexpr int NSP = I / RPWH;                 // shared gate/up items
+  constexpr int CRQ = H / 32;                   // 16-byte router chunks per quarter row
+  constexpr int CPLR = (CRQ + 63) / 64;
+  constexpr int PW = QTraits<BITS>::PW;
+  constexpr int PER_L = (kFusedMaxE + kLB - 1) / kLB;
+  constexpr int kSlots = 1 + MAXR;
+
   const int NB = gridDim.x, wg = blockIdx.x;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rank = wv * NB + wg;
   const int W = NB * kLW;
-  const int E = A.E, K = A.K, H = A.H, I = A.I;
+  const int E = A.E, K = A.K;
+  const int glh = lane % LGH, subh = lane / LGH;
+  const int gli = lane % LGI, subi = lane / LGI;
+  const int row0 = wg * kRB;
 
-  __shared__ float s_hs[kFusedMaxI];
-  __shared__ float s_hr[kFusedMaxK * kFusedMaxI];
-  __shared__ float s_y[kFusedMaxK + 1][2 * kLW * 8];
+  __shared__ uint32_t s_xp[CH * PW];
+  __shared__ float s_xsc[CH], s_xsum[CH];
+  __shared__ float s_h[(kFusedMaxK + 1) * I];   // routed h (k < K), shared h (k = K)
+  __shared__ float s_y[kFusedMaxK + 1][kRB];
+  __shared__ float s_part[kLW];
   __shared__ int s_idx[kFusedMaxK];
   __shared__ float s_w[kFusedMaxK];
-  __shared__ float s_gamma;
+  __shared__ uint32_t s_tag;
   __shared__ float s_rv[kLW];
-  __shared__ int s_ri[kLW];
-
-  const uint32_t tag = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  __shared__ uint64_t s_key[kFusedMaxE + 16 * kLW];
+  __shared__ uint64_t s_ck[kLW * kFusedMaxK];
+  __shared__ uint4 s_dq[kLW * kSlots * 64];     // down-row codes fetched by LDS DMA
+  __shared__ uint32_t s_ds[kLW * kSlots * 64];  // their scale/bias words
   bool ok_all = true;
 
-  const int Ch = H * BITS / 128, Gh = H / kGroup;
-  const int64_t rbh = (int64_t)H * BITS / 8;
-  const int Ci = I * BITS / 128, Gi = I / kGroup;
-  const int64_t rbi = (int64_t)I * BITS / 8;
+  uint32_t epoch = 0;
+  if (threadIdx.x == 0)
+    epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // output rows owned by this workgroup
-  const int row0 = wg * A.RB;
-  const int nrows = max(0, min(A.RB, H - row0));
-  const int ditems = (nrows + RPWI - 1) / RPWI;
-  const float resid = (int)threadIdx.x < nrows ? A.residual[row0 + threadIdx.x] : 0.f;
+  // ---- 1. loads: router rows, one shared gate/up pair, shared down rows (DMA)
+  const int quarter = wv & 3;
+  uint4 rq[CPLR];
+  float rx[CPLR][8];
+  auto router_fetch = [&](int row) {
+#pragma unroll
+    for (int i = 0; i < CPLR; ++i) {
+      const int cq = lane + 64 * i;
+      const int c = quarter * CRQ + cq;
+      const bool ok = row < E && cq < CRQ;
+      rq[i] = ok ? reinterpret_cast<const uint4*>(A.router + (int64_t)row * H)[c]
+                 : make_uint4(0u, 0u, 0u, 0u);
+      float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
+      if (ok) {
+        f0 = reinterpret_cast<const float4*>(A.x + 8 * c)[0];
+        f1 = reinterpret_cast<const float4*>(A.x + 8 * c)[1];
+      }
+      rx[i][0] = f0.x; rx[i][1] = f0.y; rx[i][2] = f0.z; rx[i][3] = f0.w;
+      rx[i][4] = f1.x; rx[i][5] = f1.y; rx[i][6] = f1.z; rx[i][7] = f1.w;
+    }
+  };
+  router_fetch(wg * 2 + (wv >> 2));
 
-  // ---- prefetch: this wave's shared-expert down rows (known before anything runs)
-  const int gli = lane % LGI, subi = lane / LGI;
-  RowDot<BITS, LGI, 1> dI;
-  uint4 q_sd[1][1];
-  uint32_t s_sd[1][1];
+  const bool has_sp = rank < NSP;
+  const int jsp = rank * RPWH + subh;
+  uint4 qsp[2][CPLH];
+  uint32_t ssp[2][CPLH];
+  RowDot<BITS, LGH, CPLH> dH;
   {
-    const int nl = wv * RPWI + subi;
-    const bool ok = wv < ditems && nl < nrows;
-    const uint8_t* cr = A.sblk + A.off_d + (int64_t)(row0 + nl) * rbi;
-    const uint32_t* sr = reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)(row0 + nl) * Gi;
-    dI.template fetch<1>(&cr, &sr, &ok, Ci, gli, q_sd, s_sd);
+    const uint8_t* cr[2] = {A.sblk + A.off_g + jsp * RBH, A.sblk + A.off_u + jsp * RBH};
+    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + jsp * GH,
+                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + jsp * GH};
+    const bool ok[2] = {has_sp, has_sp};
+    dH.template fetch<2>(cr, sr, ok, CH, glh, qsp, ssp);
+  }
+  // shared-expert down rows of this workgroup: slot 0 of waves 0..DITEMS-1
+  const int nl_s = wv * RPWI + subi;
+  const bool sd_ok = wv < DITEMS && nl_s < kRB && row0 + nl_s < H;
+  if (sd_ok) {
+    const int sl = wv * kSlots;
+    dma16(A.sblk + A.off_d + (row0 + nl_s) * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
+    dma4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (row0 + nl_s) * GI +
+             gli / QTraits<BITS>::CPG,
+         lds_ptr(&s_ds[sl * 64]));
+  }
+  const float resid = (int)threadIdx.x < kRB ? A.residual[row0 + threadIdx.x] : 0.f;
+  uint4 gq = make_uint4(0u, 0u, 0u, 0u);  // shared-gate vector chunk for gamma (step 8)
+  float gx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if ((int)threadIdx.x < H / 8) {
+    gq = reinterpret_cast<const uint4*>(A.g)[threadIdx.x];
+    const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[0];
+    const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[1];
+    gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
+    gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
   }
 
-  // ---- phase A: router rows, shared gate/up rows (the host sizes the grid so that
-  // every phase-A row has its own wave: E + 1 + I/RPWH <= waves)
-  const int glh = lane % LGH, subh = lane / LGH;
-  const int n_sp = I / RPWH;
-  if (rank <= E) {
-    const uint16_t* row = rank < E ? A.router + (int64_t)rank * H : A.g;
+  // ---- 2. router dots -> logits (the writers, threads 0 and 1, are in the same
+  //         wave as the epoch reader, so the tag needs no barrier)
+  const uint32_t tag0 = (uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u;
+  for (int r0 = wg * 2; r0 < E; r0 += NB * 2) {
+    if (r0 != wg * 2) router_fetch(r0 + (wv >> 2));
     float acc = 0.f;
 #pragma unroll
-    for (int h0 = 0; h0 < CPLR; h0 += 4) {  // four 16-byte chunks in flight per step
-      uint4 q[4];
-      float xr[4][8];
-#pragma unroll
-      for (int i = 0; i < 4 && h0 + i < CPLR; ++i) {
-        const int c = lane + 64 * (h0 + i);
-        q[i] = reinterpret_cast<const uint4*>(row)[c];
-        const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * c)[0];
-        const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * c)[1];
-        xr[i][0] = f0.x; xr[i][1] = f0.y; xr[i][2] = f0.z; xr[i][3] = f0.w;
-        xr[i][4] = f1.x; xr[i][5] = f1.y; xr[i][6] = f1.z; xr[i][7] = f1.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 4 && h0 + i < CPLR; ++i) acc += bf16_chunk_dot(q[i], xr[i]);
-    }
+    for (int i = 0; i < CPLR; ++i) acc += bf16_chunk_dot(rq[i], rx[i]);
     acc = group_sum<64>(acc);
-    if (lane == 0) tag_put(A.logits + rank, acc, tag);
-  } else if (rank < E + 1 + n_sp) {
-    RowDot<BITS, LGH, CPLH> dA;
-    dA.load_x(A.x, Ch, glh);
-    const int j = (rank - E - 1) * RPWH + subh;
-    const uint8_t* cr[2] = {A.sblk + A.off_g + (int64_t)j * rbh, A.sblk + A.off_u + (int64_t)j * rbh};
-    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + (int64_t)j * Gh,
-                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + (int64_t)j * Gh};
-    const bool ok[2] = {true, true};
-    uint4 q[2][CPLH];
-    uint32_t s[2][CPLH];
-    dA.template fetch<2>(cr, sr, ok, Ch, glh, q, s);
+    if (lane == 0) s_part[wv] = acc;
+    __syncthreads();
+    if (threadIdx.x < 2 && r0 + (int)threadIdx.x < E) {
+      const float* pp = s_part + 4 * threadIdx.x;
+      tag_put(A.logits + r0 + threadIdx.x, (pp[0] + pp[1]) + (pp[2] + pp[3]), tag0);
+    }
+    __syncthreads();
+  }
+
+  // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
+  prep_x_coop<BITS>(A.x, H, s_xp, s_xsc, s_xsum, threadIdx.x, kLB);
+  if (threadIdx.x == 0) s_tag = tag0;
+  __syncthreads();
+  const uint32_t tag = s_tag;
+
+  // ---- 4. shared gate/up + SwiGLU -> hs (stored after the top-K: nothing needs it
+  //         before step 8, and a store now would be waited for by the logit poll)
+  uint64_t* hs = A.hs + (size_t)(tag % kSlotsH) * I;
+  uint64_t* hr = A.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
+  dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
+  float hs_val = 0.f;
+  if (has_sp) {
     float p[2];
-    dA.template dots<2>(q, s, p);
+    dH.template dots<2>(qsp, ssp, p);
     const float a = group_sum<LGH>(p[0]);
     const float u = group_sum<LGH>(p[1]);
-    if (glh == 0) tag_put(A.hs + j, silu_f(a) * u, tag);
+    hs_val = silu_f(a) * u;
   }
 
-  // ---- shared h -> LDS, shared down rows (prefetched codes)
-  ok_all &= poll_to_lds<(kFusedMaxI + kLB - 1) / kLB>(A.hs, I, tag, s_hs);
-  __syncthreads();
-  if (wv < ditems) {
-    dI.load_x(s_hs, Ci, gli);
-    float p[1];
-    dI.template dots<1>(q_sd, s_sd, p);
-    const float v = group_sum<LGI>(p[0]);
-    const int nl = wv * RPWI + subi;
-    if (gli == 0 && nl < nrows) s_y[K][nl] = v;
-  }
-
-  // ---- phase B: top-K from the logits (every workgroup), ties to the lower index
+  // ---- 5. top-K by ranking 64-bit keys (order: larger value, then lower index)
   {
     float lv[PER_L];
-    {
-      uint32_t pending = 0;
+    uint32_t pending = 0;
+#pragma unroll
+    for (int j = 0; j < PER_L; ++j)
+      if ((int)threadIdx.x + j * kLB < E) pending |= 1u << j;
+    for (uint32_t spins = 0; pending; ++spins) {
+      uint64_t v[PER_L];
 #pragma unroll
       for (int j = 0; j < PER_L; ++j)
-        if ((int)threadIdx.x + j * kLB <= E) pending |= 1u << j;
-      for (uint32_t spins = 0; pending; ++spins) {
-        uint64_t v[PER_L];
+        v[j] = (pending >> j) & 1u ? tag_get(A.logits + threadIdx.x + j * kLB) : 0;
 #pragma unroll
-        for (int j = 0; j < PER_L; ++j)
-          v[j] = (pending >> j) & 1u ? tag_get(A.logits + threadIdx.x + j * kLB) : 0;
-#pragma unroll
-        for (int j = 0; j < PER_L; ++j)
-          if (((pending >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
-            lv[j] = __uint_as_float((uint32_t)v[j]);
-            pending &= ~(1u << j);
-          }
-        if (!pending) break;
-        if (spins > kSpinLimit) {
-          ok_all = false;
-          break;
+      for (int j = 0; j < PER_L; ++j)
+        if (((pending >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
+          lv[j] = __uint_as_float((uint32_t)v[j]);
+          pending &= ~(1u << j);
         }
-        __builtin_amdgcn_s_sleep(1);
+      if (!pending) break;
+      if (spins > kSpinLimit) {
+        ok_all = false;
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    if ((int)threadIdx.x == E % kLB) s_gamma = sigmoid_f(lv[E / kLB]);
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-      float bv = 0.f;
-      int bi = -1;
+    // Wave w owns the block of keys [w*EB, w*EB + EB) (EB a multiple of 16; the
+    // padding is zero and never wins).  Each lane counts the keys of its block
+    // that beat its own; the K best of every block are candidates, and wave 0
+    // ranks the 8K candidates the same way.  Rank r < K is the r-th expert.
+    const int EB = ((E + kLW - 1) / kLW + 15) & ~15;
 #pragma unroll
-      for (int j = 0; j < PER_L; ++j) {
-        const int e = threadIdx.x + j * kLB;
-        if (e < E && !((taken >> j) & 1u) && better(lv[j], e, bv, bi)) {
-          bv = lv[j];
-          bi = e;
-        }
+    for (int j = 0; j < PER_L; ++j) {
+      const int e = threadIdx.x + j * kLB;
+      if (e < E) s_key[e] = sort_key(lv[j], e);
+    }
+    for (int q = E + threadIdx.x; q < kLW * EB; q += kLB) s_key[q] = 0;
+    if (threadIdx.x < kLW * kFusedMaxK) s_ck[threadIdx.x] = 0;
+    __syncthreads();
+    const int b0 = wv * EB;
+    const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(s_key + b0);
+    for (int e = b0 + lane; e < b0 + EB; e += 64) {
+      const uint64_t key = s_key[e];
+      int r0 = 0, r1 = 0;
+#pragma unroll 8
+      for (int q = 0; q < EB / 2; ++q) {  // broadcast reads: every lane reads the same words
+        const ulonglong2 kk = kb[q];
+        r0 += kk.x > key ? 1 : 0;
+        r1 += kk.y > key ? 1 : 0;
       }
+      const int rk = r0 + r1;
+      if (key != 0 && rk < K) s_ck[wv * kFusedMaxK + rk] = key;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const uint64_t key = lane < kLW * kFusedMaxK ? s_ck[lane] : 0;
+      int rk = 0;
+      const ulonglong2* cb = reinterpret_cast<const ulonglong2*>(s_ck);
 #pragma unroll
-      for (int m = 32; m > 0; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (oi >= 0 && better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
+      for (int q = 0; q < kLW * kFusedMaxK / 2; ++q) {
+        const ulonglong2 kk = cb[q];
+        rk += (kk.x > key ? 1 : 0) + (kk.y > key ? 1 : 0);
       }
+      if (key != 0 && rk < K) {
+        s_idx[rk] = (int)(0xFFFFFFFFu - (uint32_t)key);
+        s_w[rk] = key_value(key);  // logit for now
+      }
+      // thread 0 belongs to wave 0: no barrier between the ranks and the softmax
       if (lane == 0) {
-        s_rv[wv] = bv;
-        s_ri[wv] = bi;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        float b = s_rv[0];
-        int i = s_ri[0];
-        for (int q = 1; q < kLW; ++q)
-          if (s_ri[q] >= 0 && better(s_rv[q], s_ri[q], b, i)) {
-            b = s_rv[q];
-            i = s_ri[q];
-          }
-        s_idx[k] = i;
-        s_w[k] = b;  // logit for now
-      }
-      __syncthreads();
-      const int won = s_idx[k];
-      if (won >= 0 && won % kLB == (int)threadIdx.x) taken |= 1u << (won / kLB);
-    }
-    if (threadIdx.x == 0) {
-      const float m = s_w[0];
-      float ex[kFusedMaxK];
-      float sum = 0.f;
-      for (int k = 0; k < K; ++k) {
-        ex[k] = expf(s_w[k] - m);
-        sum += ex[k];
-      }
-      const float inv = 1.0f / sum;
-      for (int k = 0; k < K; ++k) s_w[k] = ex[k] * inv;
-      if (wg == 0) {
-        for (int k = 0; k < K; ++k) {
-          A.idx_out[k] = s_idx[k];
-          A.w_out[k] = s_w[k];
+        const float m = s_w[0];
+        float ex[kFusedMaxK];
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < kFusedMaxK; ++k) {
+          ex[k] = k < K ? __expf(s_w[k] - m) : 0.f;
+          sum += ex[k];
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int k = 0; k < kFusedMaxK; ++k)
+          if (k < K) s_w[k] = ex[k] * inv;
+        if (wg == 0) {
+#pragma unroll
+          for (int k = 0; k < kFusedMaxK; ++k)
+            if (k < K) {
+              A.idx_out[k] = s_idx[k];
+              A.w_out[k] = s_w[k];
+            }
         }
       }
     }
     __syncthreads();
   }
-
-  // ---- prefetch: this wave's routed down rows for phase C
-  uint4 q_rd[kMaxRoutedItems][1];
-  uint32_t s_rd[kMaxRoutedItems][1];
+  int eidx[kFusedMaxK];
 #pragma unroll
-  for (int m = 0; m < kMaxRoutedItems; ++m) {
-    const int t = wv * kMaxRoutedItems + m;
-    const int k = ditems > 0 ? t / ditems : 0, d = ditems > 0 ? t % ditems : 0;
-    const int e = t < K * ditems ? s_idx[k] : -1;
-    const int nl = d * RPWI + subi;
-    const bool ok = (unsigned)e < (unsigned)E && nl < nrows;
-    const uint8_t* blk = A.rbase + (ok ? (int64_t)e * A.rstride : 0);
-    const uint8_t* cr = blk + A.off_d + (int64_t)(row0 + nl) * rbi;
-    const uint32_t* sr = reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)(row0 + nl) * Gi;
-    uint4 qq[1][1];
-    uint32_t ss[1][1];
-    dI.template fetch<1>(&cr, &sr, &ok, Ci, gli, qq, ss);
-    q_rd[m][0] = qq[0][0];
-    s_rd[m][0] = ss[0][0];
-  }
+  for (int k = 0; k < kFusedMaxK; ++k) eidx[k] = k < K ? s_idx[k] : -1;
+  if (has_sp && glh == 0) tag_put(hs + jsp, hs_val, tag);
 
-  // ---- phase B: routed gate/up rows + SwiGLU
-  RowDot<BITS, LGH, CPLH> dH;
-  dH.load_x(A.x, Ch, glh);
-  const int n_rp = K * n_sp;
-  // two row pairs per step so that four rows of codes are in flight per wave
-  for (int it = rank; it < n_rp; it += 2 * W) {
+  // ---- 6. loads: two routed gate/up row pairs per wave, then the routed down rows
+  //         of this workgroup's output rows (LDS DMA, slots 1..MAXR)
+  const int n_rp = K * NSP;
+  int it = rank;
+  uint4 q[4][CPLH];
+  uint32_t sq[4][CPLH];
+  int kk[2], jj[2];
+  bool eok[2];
+  auto fetch_pairs = [&](int it0) {
     const uint8_t* cr[4];
     const uint32_t* sr[4];
     bool ok[4];
-    int kk[2], jj[2];
-    bool eok[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const int item = it + v * W;
+      const int item = it0 + v * W;
       const bool valid = item < n_rp;
-      kk[v] = valid ? item / n_sp : 0;
-      jj[v] = valid ? (item % n_sp) * RPWH + subh : 0;
-      const int e = valid ? s_idx[kk[v]] : -1;
+      kk[v] = valid ? item / NSP : 0;
+      jj[v] = valid ? (item % NSP) * RPWH + subh : 0;
+      int e = -1;
+#pragma unroll
+      for (int k = 0; k < kFusedMaxK; ++k)
+        if (valid && kk[v] == k) e = eidx[k];
       eok[v] = (unsigned)e < (unsigned)E;
       const uint8_t* blk = A.rbase + (eok[v] ? (int64_t)e * A.rstride : 0);
-      cr[2 * v] = blk + A.off_g + (int64_t)jj[v] * rbh;
-      cr[2 * v + 1] = blk + A.off_u + (int64_t)jj[v] * rbh;
-      sr[2 * v] = reinterpret_cast<const uint32_t*>(blk + A.off_gsb) + (int64_t)jj[v] * Gh;
-      sr[2 * v + 1] = reinterpret_cast<const uint32_t*>(blk + A.off_usb) + (int64_t)jj[v] * Gh;
+      cr[2 * v] = blk + A.off_g + jj[v] * RBH;
+      cr[2 * v + 1] = blk + A.off_u + jj[v] * RBH;
+      sr[2 * v] = reinterpret_cast<const uint32_t*>(blk + A.off_gsb) + jj[v] * GH;
+      sr[2 * v + 1] = reinterpret_cast<const uint32_t*>(blk + A.off_usb) + jj[v] * GH;
       ok[2 * v] = ok[2 * v + 1] = eok[v];
     }
-    uint4 q[4][CPLH];
-    uint32_t s[4][CPLH];
-    dH.template fetch<4>(cr, sr, ok, Ch, glh, q, s);
+    dH.template fetch<4>(cr, sr, ok, CH, glh, q, sq);
+  };
+  if (it < n_rp) fetch_pairs(it);
+  uint32_t slot_ok = sd_ok ? 1u : 0u;
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) {
+    const int t = wv * MAXR + m;
+    const int k = t / DITEMS, d = t % DITEMS;
+    const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
+    const int nl = d * RPWI + subi;
+    const bool ok = (unsigned)e < (unsigned)E && nl < kRB && row0 + nl < H;
+    if (ok) {
+      const uint8_t* blk = A.rbase + (int64_t)e * A.rstride;
+      const int sl = wv * kSlots + 1 + m;
+      dma16(blk + A.off_d + (row0 + nl) * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
+      dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (row0 + nl) * GI +
+               gli / QTraits<BITS>::CPG,
+           lds_ptr(&s_ds[sl * 64]));
+      slot_ok |= 2u << m;
+    }
+  }
+
+  // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step
+  for (; it < n_rp; it += 2 * W) {
+    if (it != rank) fetch_pairs(it);
     float p[4];
-    dH.template dots<4>(q, s, p);
+    dH.template dots<4>(q, sq, p);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const float a = group_sum<LGH>(p[2 * v]);
       const float u = group_sum<LGH>(p[2 * v + 1]);
       if (glh == 0 && it + v * W < n_rp)
-        tag_put(A.hr + (int64_t)kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
+        tag_put(hr + kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
     }
   }
-
-  // ---- phase C: routed h -> LDS, down rows, combine
-  ok_all &= poll_to_lds<(kFusedMaxK * kFusedMaxI + kLB - 1) / kLB>(A.hr, K * I, tag, s_hr);
+  // completion: every store of this workgroup acknowledged, then one tagged flag
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // Workgroup 0 has now seen outputs of every wave of the grid (logits, hs, hr),
-  // so every wave has read the epoch: advance it for the next call.
+  if (threadIdx.x == 0) tag_put(A.flags + wg, 0.f, tag);
+
+  // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
+  //         routed down rows (float dots from h in LDS, codes from the LDS DMA);
+  //         combine
+  if ((int)threadIdx.x < NB) {
+    uint32_t spins = 0;
+    while ((uint32_t)(tag_get(A.flags + threadIdx.x) >> 32) != tag) {
+      if (++spins > kSpinLimit) {
+        ok_all = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  // Every workgroup has read the epoch before tagging its flag: advance it.
   if (wg == 0 && threadIdx.x == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int prev_k = -1;
+  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB>(hr, K * I, tag, s_h);
+  read_done_to_lds<(I + kLB - 1) / kLB>(hs, I, tag, s_h + kFusedMaxK * I);
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 6) has landed
+  const float gpart = group_sum<64>(bf16_chunk_dot(gq, gx));
+  if (lane == 0) s_rv[wv] = gpart;
+  RowDotF<BITS, LGI> dF;
+  if (wv < DITEMS) {
+    dF.load_x(s_h + kFusedMaxK * I, CI, gli);
+    const int sl = wv * kSlots;
+    const float v = group_sum<LGI>(dF.dot(sd_ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u),
+                                          sd_ok ? s_ds[sl * 64 + lane] : 0u));
+    if (gli == 0 && nl_s < kRB) s_y[kFusedMaxK][nl_s] = v;
+  }
 #pragma unroll
-  for (int m = 0; m < kMaxRoutedItems; ++m) {
-    const int t = wv * kMaxRoutedItems + m;
-    if (t < K * ditems) {
-      const int k = t / ditems, d = t % ditems;
-      if (k != prev_k) {
-        dI.load_x(s_hr + k * I, Ci, gli);
-        prev_k = k;
-      }
-      uint4 qq[1][1] = {{q_rd[m][0]}};
-      uint32_t ss[1][1] = {{s_rd[m][0]}};
-      float p[1];
-      dI.template dots<1>(qq, ss, p);
-      const float v = group_sum<LGI>(p[0]);
+  for (int m = 0; m < MAXR; ++m) {
+    const int t = wv * MAXR + m;
+    if (t < K * DITEMS) {
+      const int k = t / DITEMS, d = t % DITEMS;
+      if (m == 0 || d == 0) dF.load_x(s_h + k * I, CI, gli);  // a new expert for this wave
+      const bool ok = (slot_ok >> (1 + m)) & 1u;
+      const int sl = wv * kSlots + 1 + m;
+      const float v = group_sum<LGI>(dF.dot(ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u),
+                                            ok ? s_ds[sl * 64 + lane] : 0u));
       const int nl = d * RPWI + subi;
-      const int e = s_idx[k];
-      if (gli == 0 && nl < nrows) s_y[k][nl] = (unsigned)e < (unsigned)E ? v : __builtin_nanf("");
+      const bool eok_k = (unsigned)eidx[k < kFusedMaxK ? k : 0] < (unsigned)E;
+      if (gli == 0 && nl < kRB) s_y[k][nl] = eok_k ? v : __builtin_nanf("");
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < nrows) {
+  if ((int)threadIdx.x < kRB && row0 + (int)threadIdx.x < H) {
+    float gs = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) gs += s_rv[w];
     float acc = resid;
     for (int k = 0; k < K; ++k) acc = fmaf(s_w[k], s_y[k][threadIdx.x], acc);
-    A.out[row0 + threadIdx.x] = fmaf(s_gamma, s_y[K][threadIdx.x], acc);
+    A.out[row0 + threadIdx.x] = fmaf(sigmoid_f(gs), s_y[kFusedMaxK][threadIdx.x], acc);
   }
   if (!ok_all) flag_status(A.ctrl, 1u);
 }
@@ -413,16 +531,17 @@ struct FusedCfg {
 inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 struct WsLayout {
-  int64_t ctrl, logits, hs, hr, total;
+  int64_t ctrl, logits, flags, hs, hr, total;
 };
 
-WsLayout fused_ws(int E, int K, int I) {
+WsLayout fused_ws(int E, int H, int I) {
   WsLayout w;
   w.ctrl = 0;
   w.logits = 256;
-  w.hs = w.logits + align256((int64_t)(E + 1) * 8);
-  w.hr = w.hs + align256((int64_t)I * 8);
-  w.total = w.hr + align256((int64_t)K * I * 8);
+  w.flags = w.logits + align256((int64_t)E * 8);
+  w.hs = w.flags + align256((int64_t)(H / kRB) * 8);
+  w.hr = w.hs + align256((int64_t)kSlotsH * I * 8);
+  w.total = w.hr + align256((int64_t)kSlotsH * kFusedMaxK * I * 8);
   return w;
 }
 
@@ -445,13 +564,7 @@ using KernelFn = void (*)(LayerArgs);
 
 template <int BITS, int H, int I>
 KernelFn pick() {
-  constexpr int CH = H * BITS / 128;
-  constexpr int LGH = CH >= 64 ? 64 : CH;
-  constexpr int CPLH = CH >= 64 ? CH / 64 : 1;
-  constexpr int CI = I * BITS / 128;
-  constexpr int LGI = CI >= 64 ? 64 : CI;
-  static_assert(CI <= 64, "down rows must fit one chunk per lane");
-  return k_layer<BITS, LGH, CPLH, LGI, H / 512>;
+  return k_layer<BITS, H, I>;
 }
 
 template <int BITS, int H>
@@ -474,7 +587,7 @@ KernelFn pick_h(int H, int I) {
 FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
-  if (!fn || K > kFusedMaxK || E > kFusedMaxE || I > kFusedMaxI) return c;
+  if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return c;
   static int cus[64] = {0};  // per-device CU count; concurrent first calls store equal values
@@ -489,23 +602,17 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
                                                    kLB, 0) != hipSuccess ||
       blocks_per_cu < 1)
     return c;
-  int nb = cus[dev] * (blocks_per_cu < 2 ? blocks_per_cu : 2);
-  // every wave must own at least one phase-A or phase-B row (epoch hand-over)
+  const int nb = H / kRB;
+  if (nb > cus[dev] * blocks_per_cu) return c;  // every workgroup must be resident at once
   const int bits = L.routed.bits;
   const int ch = H * bits / 128;
   const int rpwh = 64 / (ch >= 64 ? 64 : ch);
   const int n_sp = I / rpwh;
-  const int n_items = (E + 1 + n_sp) > K * n_sp ? (E + 1 + n_sp) : K * n_sp;
-  if (nb * kLW > n_items) nb = n_items / kLW;
-  if (nb < 1 || nb * kLW < E + 1 + n_sp) return c;  // one phase-A row per wave
-  const int ci = I * bits / 128;
-  const int rpwi = 64 / (ci >= 64 ? 64 : ci);
-  int rb = (H + nb - 1) / nb;
-  rb = (rb + rpwi - 1) / rpwi * rpwi;
-  const int ditems = rb / rpwi;
-  if (ditems > kLW || K * ditems > kLW * kMaxRoutedItems || rb > 2 * kLW * 8) return c;
+  // one shared gate/up item per wave at most, and every workgroup must tag a routed
+  // h row (rank == workgroup index) for the epoch hand-over
+  if (n_sp > nb * kLW || K * n_sp < nb) return c;
   c.nb = nb;
-  c.rb = rb;
+  c.rb = kRB;
   return c;
 }
 
@@ -518,7 +625,7 @@ KernelFn fused_kernel(const qmoe_layer& L) {
 
 size_t layer_workspace_bytes(const qmoe_layer& L) {
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
-  const WsLayout f = fused_ws(E, K, I);
+  const WsLayout f = fused_ws(E, H, I);
   const UnfusedWs u = unfused_ws(E, K, H, I);
   return (size_t)(f.total > u.total ? f.total : u.total);
 }
@@ -530,7 +637,7 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residu
   KernelFn fn = fused_kernel(L);
   const FusedCfg cfg = fused_config(L, fn);
   if (cfg.nb > 0) {
-    const WsLayout wl = fused_ws(E, K, I);
+    const WsLayout wl = fused_ws(E, H, I);
     const qmoe_expert_offsets o = expert_offsets(H, I, L.routed.bits);
     LayerArgs A;
     A.rbase = static_cast<const uint8_t*>(L.routed.base);
@@ -551,13 +658,11 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residu
     A.w_out = w;
     A.ctrl = reinterpret_cast<uint32_t*>(wsb + wl.ctrl);
     A.logits = reinterpret_cast<uint64_t*>(wsb + wl.logits);
+    A.flags = reinterpret_cast<uint64_t*>(wsb + wl.flags);
     A.hs = reinterpret_cast<uint64_t*>(wsb + wl.hs);
     A.hr = reinterpret_cast<uint64_t*>(wsb + wl.hr);
     A.E = E;
     A.K = K;
-    A.H = H;
-    A.I = I;
-    A.RB = cfg.rb;
     hipLaunchKernelGGL(fn, dim3(cfg.nb), dim3(kLB), 0, s, A);
     return hipGetLastError();
   }

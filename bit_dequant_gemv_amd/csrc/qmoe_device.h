@@ -2,26 +2,37 @@
 //
 // Quantized row dot product.  The page "flash-moe 소개" (discuss.pytorch.kr),
 // section "FMA 최적화 역양자화 커널", rewrites (nibble*scale + bias)*x as
-// fma(nibble, scale*x, bias*x) so that the inner loop is one FMA per weight.
-// Here the same identity is taken one step further, per group of 64 inputs:
+// fma(nibble, scale*x, bias*x) so that the dequantisation costs no extra
+// instruction per weight.  Here the same identity is applied per group of 64
+// inputs,
 //
-//     sum_k (q_k s + b) x_k  =  s * sum_k q_k x_k  +  b * sum_k x_k
+//     sum_k (q_k s + b) x_k  =  s * sum_k q_k x_k  +  b * sum_k x_k ,
 //
-// sum_k x_k of a lane's inputs is fixed for a whole matrix, so the inner loop is
-// one code conversion and one FMA per weight, and scale and bias cost two FMAs
-// per 32 (4-bit) or 64 (2-bit) weights.
+// so scale and bias cost two FMAs per 32 (4-bit) or 64 (2-bit) weights, and the
+// inner sum sum_k q_k x_k is computed with integer dot instructions instead of
+// per-weight float conversions:
 //
-// Work split: a "lane group" of LG lanes (a power of two <= 64) owns one row at
-// a time; lane gl of the group owns the 16-byte chunks gl, gl+LG, ... (CPL of
-// them) of every row, so its slice of x is loop-invariant and lives in VGPRs,
-// pre-scaled so that a code can be converted straight from its byte position:
-//   4-bit: a chunk holds 32 codes.  w & 0x0F0F0F0F leaves the even codes as
-//          bytes, w & 0xF0F0F0F0 leaves 16 * (odd codes) as bytes; each byte
-//          becomes a float in one v_cvt_f32_ubyteN, and the odd x are stored
-//          divided by 16 (exact).
-//   2-bit: a chunk holds 64 codes = one group; masks 0x03.., 0x0C.., 0x30..,
-//          0xC0.. leave 4^m * code; the matching x are stored divided by 4^m.
-// The per-row partial sums of a group are combined with xor shuffles.
+//   * Each 16-byte chunk of a row (32 four-bit or 64 two-bit codes) meets a
+//     chunk of x that a lane keeps for the whole matrix.  That x chunk is put in
+//     24-bit block fixed point: E is chosen so that |x_k| < 2^E for the chunk,
+//     X_k = rint(x_k * 2^(22-E)) (|X_k| <= 2^22) and U_k = X_k + 2^23 lies in
+//     [0, 2^24).  U_k is split into six 4-bit digits ("planes").
+//   * v_dot8_u32_u4 multiplies eight packed 4-bit codes by eight 4-bit digits and
+//     accumulates in 32 bits, exactly.  Six planes give sum_k q_k U_k; one more dot
+//     with 0x11111111 gives sum_k q_k, which removes the 2^23 offset.  Nothing is
+//     rounded until the per-chunk integer totals are converted to float.
+//   * 4-bit codes are used as they sit in memory.  2-bit codes are spread to
+//     nibbles with two masks ((w & 0x33333333) << 2 and w & 0xCCCCCCCC), which
+//     multiplies every code by 4; the chunk scale carries the 1/4.
+// Cost: 7 dot instructions per 8 four-bit codes plus ~14 instructions per chunk,
+// about 1.3 VALU instructions per weight, against 2.25 for one float conversion
+// and one FMA per weight.  Accuracy: the x chunk keeps 23 significant bits
+// relative to its largest element; the integer sums are exact.
+//
+// Work split: a "lane group" of LG lanes (a power of two <= 64) owns one row at a
+// time; lane gl of the group owns the 16-byte chunks gl, gl+LG, ... (CPL of them)
+// of every row, so its x planes are loop-invariant and live in VGPRs.  Partial
+// row sums of a group are combined with xor shuffles.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,62 +48,259 @@ template <>
 struct QTraits<4> {
   static constexpr int EPC = 32;  // codes per 16-byte chunk
   static constexpr int CPG = 2;   // chunks per group of 64
+  static constexpr int EPW = 8;   // codes per 32-bit word
+  static constexpr int PW = 24;   // plane words per chunk: 4 code words x 6 digits
+  static constexpr float FACTOR = 1.0f;
 };
 template <>
 struct QTraits<2> {
   static constexpr int EPC = 64;
   static constexpr int CPG = 1;
+  static constexpr int EPW = 16;
+  static constexpr int PW = 48;   // 4 code words x 2 nibble halves x 6 digits
+  static constexpr float FACTOR = 0.25f;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// byte j of v as a float (the backend selects v_cvt_f32_ubyteJ)
-__device__ __forceinline__ float ubyte_f(uint32_t v, int j) {
-  return (float)((v >> (8 * j)) & 0xFFu);
-}
-
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-// sum over aligned groups of LG lanes (LG a power of two <= 64)
+__device__ __forceinline__ uint32_t udot8(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_udot8(a, b, c, false);
+}
+
+// Cross-lane moves without LDS round trips: DPP within 16-lane rows and
+// readlane across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over aligned groups of LG lanes (LG a power of two <= 64).  The result is
+// valid in the group's first lane (and, for LG <= 16, in every lane of the group).
 template <int LG>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = LG >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (LG >= 2) v += dpp_f<kDppXor1>(v);
+  if (LG >= 4) v += dpp_f<kDppXor2>(v);
+  if (LG >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (LG >= 16) v += dpp_f<kDppMirror>(v);
+  if (LG == 32) {
+    const float a = readlane_f(v, 0) + readlane_f(v, 16);
+    const float b = readlane_f(v, 32) + readlane_f(v, 48);
+    v = (threadIdx.x & 32) ? b : a;
+  } else if (LG == 64) {
+    v = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+  }
   return v;
 }
 
-// dot of one 16-byte chunk of codes with the matching pre-scaled x
-template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint4 c, const float* xr);
+// Fixed-point parameters of a chunk with largest magnitude m: f = 2^(22-E) and
+// scale = 2^(E-22) where 2^E > m.  A zero (or negligibly small, < 2^-105) chunk
+// gets f = scale = 0; a chunk holding Inf/NaN gets scale = NaN.
+__device__ __forceinline__ void chunk_exp(float m, float& f, float& scale) {
+  const uint32_t e = (__float_as_uint(m) >> 23) & 0xFFu;  // biased exponent of m >= 0
+  if (e == 255u) {
+    f = 0.f;
+    scale = __builtin_nanf("");
+  } else if (e <= 21u) {
+    f = 0.f;
+    scale = 0.f;
+  } else {
+    f = __uint_as_float((275u - e) << 23);
+    scale = __uint_as_float((e - 21u) << 23);
+  }
+}
 
-template <>
-__device__ __forceinline__ float chunk_dot<4>(const uint4 c, const float* xr) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float a0 = 0.f, a1 = 0.f;
+__device__ __forceinline__ uint32_t to_u24(float x, float f) {
+  return (uint32_t)((int)rintf(x * f) + (1 << 23));
+}
+
+// Planes of one 32-bit code word worth of x values (v: EPW values, f from chunk_exp).
+// 4-bit: out[d], d = 0..5, nibble j = digit d of element j.
+// 2-bit: out[h*6 + d]: half h = 0 pairs with (w & 0x33333333) << 2 (elements
+// 4b+0, 4b+2 of the word in nibbles 2b, 2b+1), h = 1 with w & 0xCCCCCCCC
+// (elements 4b+1, 4b+3).
+template <int BITS>
+__device__ __forceinline__ void prep_word(const float* v, float f, uint32_t* out) {
+  constexpr int EPW = QTraits<BITS>::EPW;
+  uint32_t u[EPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x0F0F0F0Fu;
-    const uint32_t hi = w[i] & 0xF0F0F0F0u;
+  for (int j = 0; j < EPW; ++j) u[j] = to_u24(v[j], f);
+  if (BITS == 4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a0 = fmaf(ubyte_f(lo, j), xr[8 * i + 2 * j], a0);
-      a1 = fmaf(ubyte_f(hi, j), xr[8 * i + 2 * j + 1], a1);
+    for (int d = 0; d < 6; ++d) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p |= ((u[j] >> (4 * d)) & 15u) << (4 * j);
+      out[d] = p;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int d = 0; d < 6; ++d) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          p |= ((u[4 * b + h] >> (4 * d)) & 15u) << (8 * b);
+          p |= ((u[4 * b + 2 + h] >> (4 * d)) & 15u) << (8 * b + 4);
+        }
+        out[h * 6 + d] = p;
+      }
     }
   }
-  return a0 + a1;
+}
+
+// Integer total of one chunk: sum_k q_k X_k (times 4 for 2-bit codes) as a float.
+__device__ __forceinline__ float combine_planes(const uint32_t (&a)[6], uint32_t qs) {
+  const uint32_t low = a[0] + (a[1] << 4) + (a[2] << 8) + (a[3] << 12) + (a[4] << 16);
+  const int top = (int)a[5] - 8 * (int)qs;
+  return fmaf((float)top, 1048576.0f, (float)(int)low);
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint4 c, const uint32_t* P);
+
+template <>
+__device__ __forceinline__ float chunk_dot<4>(const uint4 c, const uint32_t* P) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t a[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t qs = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int d = 0; d < 6; ++d) a[d] = udot8(w[i], P[6 * i + d], a[d]);
+    qs = udot8(w[i], 0x11111111u, qs);
+  }
+  return combine_planes(a, qs);
 }
 
 template <>
-__device__ __forceinline__ float chunk_dot<2>(const uint4 c, const float* xr) {
+__device__ __forceinline__ float chunk_dot<2>(const uint4 c, const uint32_t* P) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t a[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t qs = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = (w[i] & 0x33333333u) << 2;
+    const uint32_t w1 = w[i] & 0xCCCCCCCCu;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) {
+      a[d] = udot8(w0, P[12 * i + d], a[d]);
+      a[d] = udot8(w1, P[12 * i + 6 + d], a[d]);
+    }
+    qs = udot8(w0, 0x11111111u, qs);
+    qs = udot8(w1, 0x11111111u, qs);
+  }
+  return combine_planes(a, qs);
+}
+
+// Workgroup-cooperative preparation of the x planes of a whole input vector into
+// shared memory: planes[c*PW ...], scl[c] (chunk scale, 2-bit 1/4 included) and
+// xsum[c] (plain sum of the chunk's x) for chunks c < n/EPC.  Every thread of the
+// workgroup must call it (shuffles inside); nthreads a multiple of 64.
+template <int BITS>
+__device__ __forceinline__ void prep_x_coop(const float* x, int n, uint32_t* planes, float* scl,
+                                            float* xsum, int tid, int nthreads) {
+  constexpr int EPW = QTraits<BITS>::EPW;
+  constexpr int NPW = BITS == 4 ? 6 : 12;  // plane words per code word
+  const int words = n / EPW;
+  for (int w0 = 0; w0 < words; w0 += nthreads) {
+    const int w = w0 + tid;
+    const bool valid = w < words;
+    float v[EPW];
+    float m = 0.f, s = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPW; j += 4) {
+      float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (valid) f4 = *reinterpret_cast<const float4*>(x + (int64_t)w * EPW + j);
+      v[j] = f4.x;
+      v[j + 1] = f4.y;
+      v[j + 2] = f4.z;
+      v[j + 3] = f4.w;
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
+      s += (f4.x + f4.y) + (f4.z + f4.w);
+    }
+    // a chunk is 4 consecutive words = 4 consecutive lanes (one DPP quad)
+    m = fmaxf(m, dpp_f<kDppXor1>(m));
+    m = fmaxf(m, dpp_f<kDppXor2>(m));
+    s += dpp_f<kDppXor1>(s);
+    s += dpp_f<kDppXor2>(s);
+    float f, scale;
+    chunk_exp(m, f, scale);
+    if (valid) {
+      uint32_t p[NPW];
+      prep_word<BITS>(v, f, p);
+      const int c = w >> 2, i = w & 3;
+#pragma unroll
+      for (int k = 0; k < NPW; ++k) planes[c * QTraits<BITS>::PW + i * NPW + k] = p[k];
+      if (i == 0) {
+        scl[c] = scale * QTraits<BITS>::FACTOR;
+        xsum[c] = s;
+      }
+    }
+  }
+}
+
+// Float form of the chunk dot (one v_cvt_f32_ubyteN and one FMA per code), used
+// where an input vector meets too few rows to repay building its planes.  The
+// odd (4-bit) or 4^m-position (2-bit) x values are stored pre-divided by 16 or
+// 4^m (exact), so each code is converted straight from its byte position.
+__device__ __forceinline__ float ubyte_f(uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xFFu); }
+
+// Hide a masked word from the optimiser, which would otherwise fold the mask
+// into each byte extraction and lose the single-instruction conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+template <int BITS>
+__device__ __forceinline__ float xscale_f(int e) {
+  if (BITS == 4) return (e & 1) ? 0.0625f : 1.0f;
+  const int m = e & 3;
+  return m == 0 ? 1.0f : (m == 1 ? 0.25f : (m == 2 ? 0.0625f : 0.015625f));
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_f(const uint4 c, const float* xr);
+
+template <>
+__device__ __forceinline__ float chunk_dot_f<4>(const uint4 c, const float* xr) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float a[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = opaque(w[i] & 0x0F0F0F0Fu);
+    const uint32_t hi = opaque(w[i] & 0xF0F0F0F0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[(j & 1) * 2] = fmaf(ubyte_f(lo, j), xr[8 * i + 2 * j], a[(j & 1) * 2]);
+      a[(j & 1) * 2 + 1] = fmaf(ubyte_f(hi, j), xr[8 * i + 2 * j + 1], a[(j & 1) * 2 + 1]);
+    }
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot_f<2>(const uint4 c, const float* xr) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t v = w[i] & (0x03030303u << (2 * m));
+      const uint32_t v = opaque(w[i] & (0x03030303u << (2 * m)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[m] = fmaf(ubyte_f(v, j), xr[16 * i + 4 * j + m], a[m]);
     }
@@ -100,43 +308,113 @@ __device__ __forceinline__ float chunk_dot<2>(const uint4 c, const float* xr) {
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// scale applied to x element e of a chunk so the raw byte position can be used
-template <int BITS>
-__device__ __forceinline__ float xscale(int e) {
-  if (BITS == 4) return (e & 1) ? 0.0625f : 1.0f;
-  const int m = e & 3;
-  return m == 0 ? 1.0f : (m == 1 ? 0.25f : (m == 2 ? 0.0625f : 0.015625f));
-}
+// A lane's single chunk of x in float form (CPL = 1) and its row dots.
+template <int BITS, int LG>
+struct RowDotF {
+  static constexpr int EPC = QTraits<BITS>::EPC;
+  float xr[EPC];
+  float xs;
 
-// A lane's slice of x for one matrix and the dot products of its rows.
+  __device__ __forceinline__ void load_x(const float* x, int C, int gl) {
+    xs = 0.f;
+    if (gl < C) {
+      const float4* p = reinterpret_cast<const float4*>(x + gl * EPC);
+#pragma unroll
+      for (int v = 0; v < EPC / 4; ++v) {
+        const float4 f = p[v];
+        xr[4 * v + 0] = f.x * xscale_f<BITS>(4 * v + 0);
+        xr[4 * v + 1] = f.y * xscale_f<BITS>(4 * v + 1);
+        xr[4 * v + 2] = f.z * xscale_f<BITS>(4 * v + 2);
+        xr[4 * v + 3] = f.w * xscale_f<BITS>(4 * v + 3);
+        xs += (f.x + f.y) + (f.z + f.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) xr[e] = 0.f;
+    }
+  }
+
+  // lane partial of one row: s = scale|bias word of the lane's group (0 = no row)
+  __device__ __forceinline__ float dot(const uint4 q, uint32_t s) const {
+    return fmaf(bf16_lo(s), chunk_dot_f<BITS>(q, xr), bf16_hi(s) * xs);
+  }
+};
+
+// A lane's slice of x (as fixed-point planes) for one matrix, and the row dots.
 template <int BITS, int LG, int CPL>
 struct RowDot {
   static constexpr int EPC = QTraits<BITS>::EPC;
-  float xr[CPL][EPC];
+  static constexpr int PW = QTraits<BITS>::PW;
+  uint32_t P[CPL][PW];
+  float sc[CPL];
   float xs[CPL];
 
-  // x: the input vector (global or LDS), C: 16-byte chunks per row, gl: lane in group
+  // x: the input vector (global or LDS); prepares the lane's own chunks
   __device__ __forceinline__ void load_x(const float* x, int C, int gl) {
+    constexpr int EPW = QTraits<BITS>::EPW;
+    constexpr int NPW = BITS == 4 ? 6 : 12;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = gl + i * LG;
-      float s = 0.f;
       if (c < C) {
-        const float4* p = reinterpret_cast<const float4*>(x + c * EPC);
+        const float* xc = x + c * EPC;
+        float m = 0.f, s = 0.f;
 #pragma unroll
-        for (int v = 0; v < EPC / 4; ++v) {
-          const float4 f = p[v];
-          xr[i][4 * v + 0] = f.x * xscale<BITS>(4 * v + 0);
-          xr[i][4 * v + 1] = f.y * xscale<BITS>(4 * v + 1);
-          xr[i][4 * v + 2] = f.z * xscale<BITS>(4 * v + 2);
-          xr[i][4 * v + 3] = f.w * xscale<BITS>(4 * v + 3);
-          s += (f.x + f.y) + (f.z + f.w);
+        for (int j = 0; j < EPC; j += 4) {
+          const float4 f4 = *reinterpret_cast<const float4*>(xc + j);
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
+          s += (f4.x + f4.y) + (f4.z + f4.w);
         }
+        float f, scale;
+        chunk_exp(m, f, scale);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          float v[EPW];
+#pragma unroll
+          for (int j = 0; j < EPW; j += 4) {
+            const float4 f4 = *reinterpret_cast<const float4*>(xc + wd * EPW + j);
+            v[j] = f4.x;
+            v[j + 1] = f4.y;
+            v[j + 2] = f4.z;
+            v[j + 3] = f4.w;
+          }
+          prep_word<BITS>(v, f, &P[i][wd * NPW]);
+        }
+        sc[i] = scale * QTraits<BITS>::FACTOR;
+        xs[i] = s;
       } else {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) xr[i][e] = 0.f;
+        for (int k = 0; k < PW; ++k) P[i][k] = 0u;
+        sc[i] = 0.f;
+        xs[i] = 0.f;
       }
-      xs[i] = s;
+    }
+  }
+
+  // planes prepared by prep_x_coop (shared or global memory)
+  __device__ __forceinline__ void load_prepped(const uint32_t* planes, const float* scl,
+                                               const float* xsum, int C, int gl) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = gl + i * LG;
+      if (c < C) {
+        const uint4* p = reinterpret_cast<const uint4*>(planes + c * PW);
+#pragma unroll
+        for (int k = 0; k < PW / 4; ++k) {
+          const uint4 v = p[k];
+          P[i][4 * k] = v.x;
+          P[i][4 * k + 1] = v.y;
+          P[i][4 * k + 2] = v.z;
+          P[i][4 * k + 3] = v.w;
+        }
+        sc[i] = scl[c];
+        xs[i] = xsum[c];
+      } else {
+#pragma unroll
+        for (int k = 0; k < PW; ++k) P[i][k] = 0u;
+        sc[i] = 0.f;
+        xs[i] = 0.f;
+      }
     }
   }
 
@@ -171,8 +449,8 @@ struct RowDot {
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const float d = chunk_dot<BITS>(q[r][i], xr[i]);
-        acc = fmaf(bf16_lo(s[r][i]), d, acc);
+        const float d = chunk_dot<BITS>(q[r][i], P[i]);
+        acc = fmaf(bf16_lo(s[r][i]) * sc[i], d, acc);
         acc = fmaf(bf16_hi(s[r][i]), xs[i], acc);
       }
       out[r] = acc;
