@@ -33,17 +33,18 @@ HBM_PEAK_GBPS = 8000.0
 H, I, E, K = 4096, 1024, 512, 4
 
 
-def layer_bytes(bits: int) -> int:
-    """Algorithmic HBM bytes of one batch-1 layer evaluation: router (bf16 E x H),
-    K routed + 1 shared expert blocks (codes + scale/bias), shared-gate vector,
-    x, residual and out (fp32 H each)."""
-    import oracle  # only for the byte count of an expert block (pure arithmetic)
-    return E * H * 2 + (K + 1) * oracle.expert_bytes(H, I, bits) + H * 2 + 3 * H * 4
-
-
 def expert_bytes(bits: int) -> int:
+    """Bytes of one expert block: gate, up (I x H) and down (H x I) codes plus one
+    u32 scale/bias word per row and group of 64."""
     gu = I * H * bits // 8
     return 2 * gu + H * I * bits // 8 + 4 * (2 * I * (H // 64) + H * (I // 64))
+
+
+def layer_bytes(bits: int) -> int:
+    """Algorithmic HBM bytes of one batch-1 layer evaluation: router (bf16 E x H),
+    K routed + 1 shared expert blocks, shared-gate vector (bf16 H), and x, residual
+    and out (fp32 H each)."""
+    return E * H * 2 + (K + 1) * expert_bytes(bits) + H * 2 + 3 * H * 4
 
 
 def sources_sha() -> str:
@@ -120,7 +121,10 @@ def capture_graphs(torch, fn_list, per_graph):
     return graphs
 
 
-def time_graphs(torch, graphs, n_replays, warmup_replays):
+def time_graphs(torch, graphs, n_replays, warmup_replays, tail=None):
+    """Replay graphs round-robin (plus one optional tail graph) between two
+    synchronisations; returns the seconds between the events around the timed
+    replays, recorded on the stream the graphs run on."""
     for i in range(warmup_replays):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
@@ -130,6 +134,8 @@ def time_graphs(torch, graphs, n_replays, warmup_replays):
     e0.record(st)
     for i in range(n_replays):
         graphs[i % len(graphs)].replay()
+    if tail is not None:
+        tail.replay()
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3
@@ -181,9 +187,12 @@ def run_layer_bench(args, torch, q, synth, bits):
     per_graph = 256
     calls = [(lambda t=t: q.moe_layer_forward(W.L, X[t], X[t], out, idx, w, W.ws)) for t in range(n_ring)]
     graphs = capture_graphs(torch, calls, per_graph)
-    steps = max(per_graph, (args.steps // per_graph) * per_graph)
-    warm = max(1, args.warmup // per_graph)
-    dt = time_graphs(torch, graphs, steps // per_graph, warm)
+    steps = max(1, args.steps)
+    tail = None
+    if steps % per_graph:
+        tail = capture_graphs(torch, calls[:steps % per_graph], per_graph)[0]
+    warm = (max(0, args.warmup) + per_graph - 1) // per_graph
+    dt = time_graphs(torch, graphs, steps // per_graph, warm, tail)
     status = int(W.ws[4:8].view(torch.int32).item())
     if status != 0:
         raise RuntimeError(f"fused layer kernel reported status {status}")
@@ -201,9 +210,10 @@ def run_layer_bench(args, torch, q, synth, bits):
 
 
 def run_qgemv_stream(torch, q, synth):
-    """Sustained bandwidth of the stand-alone 4-bit GEMV over matrices far larger
-    than the 256 MB last-level cache (ring of distinct 1024 x 4096 matrices)."""
-    rows, cols, n = 1024, 4096, 256
+    """Sustained bandwidth of the stand-alone 4-bit GEMV: two 131072 x 4096 matrices
+    (288 MB each with scale/bias, together above the 256 MB last-level cache) read
+    alternately.  Returns (GB/s of algorithmic bytes, average launch in us)."""
+    rows, cols, n = 131072, 4096, 2
     codes = torch.empty(n, rows, cols // 2, dtype=torch.uint8, device="cuda")
     sb = torch.empty(n, rows, cols // 64, dtype=torch.int32, device="cuda")
     synth.fill_bytes(codes, 7, 1)
@@ -212,11 +222,38 @@ def run_qgemv_stream(torch, q, synth):
     x = torch.empty(cols, dtype=torch.float32, device="cuda")
     synth.fill_normal_f32(x, 7, 3, 1.0)
     y = torch.empty(n, rows, dtype=torch.float32, device="cuda")
-    calls = [(lambda i=i: q.qgemv_w4(codes[i], sb[i], x, y[i])) for i in range(n)]
-    graphs = capture_graphs(torch, calls, 64)
-    dt = time_graphs(torch, graphs, 4 * len(graphs), 2)
-    per = rows * cols // 2 + rows * cols // 64 * 4 + cols * 4 + rows * 4
-    return per * 4 * n / dt / 1e9
+    calls = [(lambda i=i: q.qgemv_w4(codes[i % n], sb[i % n], x, y[i % n])) for i in range(16)]
+    graphs = capture_graphs(torch, calls, 16)
+    reps = 8
+    dt = time_graphs(torch, graphs, reps, 2)
+    per = rows * cols // 2 + rows * (cols // 64) * 4 + cols * 4 + rows * 4
+    launches = 16 * reps
+    del codes, sb
+    return per * launches / dt / 1e9, dt / launches * 1e6
+
+
+def run_copy(torch):
+    """Device-to-device copy of 1 GiB (read + write): the attainable-bandwidth
+    reference for this machine, and the known-size kernel that scales the HBM
+    byte counters."""
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(st)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(st)
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return 2 * 4 * n / dt / 1e9
 
 
 def main():
@@ -239,7 +276,11 @@ def main():
     torch.cuda.set_device(0)
     bits = 4 if args.config == 1 else 2
     tok_s, steps, dt, roof, extra, (seed, bits) = run_layer_bench(args, torch, q, synth, bits)
-    extra["qgemv_w4_stream_GBps"] = round(run_qgemv_stream(torch, q, synth), 1)
+    gbps, us = run_qgemv_stream(torch, q, synth)
+    extra["qgemv_w4_131072x4096_GBps"] = round(gbps, 1)
+    extra["qgemv_w4_131072x4096_frac_of_peak"] = round(gbps / HBM_PEAK_GBPS, 4)
+    extra["qgemv_w4_131072x4096_avg_launch_us"] = round(us, 2)
+    extra["copy_1GiB_GBps"] = round(run_copy(torch), 1)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_oracle_layer(seed, 0, bits, list(range(64)), args.cpu_seconds)

@@ -263,7 +263,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 
   // ---- 2. router dots -> logits (the writers, threads 0 and 1, are in the same
   //         wave as the epoch reader, so the tag needs no barrier)
-  const uint32_t tag0 = (uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u;
+  // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
+  uint32_t tag0 = (uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u;
+  tag0 = tag0 ? tag0 : 1u;
   for (int r0 = wg * 2; r0 < E; r0 += NB * 2) {
     if (r0 != wg * 2) router_fetch(r0 + (wv >> 2));
     float acc = 0.f;

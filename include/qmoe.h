@@ -117,7 +117,7 @@ int qgemv_w2(const qmoe_qmat* W, const float* x, float* y, void* stream);
  *   logits  : device float [T][E] (written; also the kernel's scratch)
  *   topk_idx: device int32 [T][K] (written): descending logit, ties to the lower index
  *   topk_w  : device float [T][K] (written): softmax over the K selected logits
- * 1 <= K <= min(E, 8), H a multiple of 64 (at most 16384), E <= 4096.
+ * 1 <= K <= min(E, 8), H a multiple of 64 (at most 8192), E <= 4096.
  */
 int moe_router_topk(const uint16_t* router, const float* x, int32_t T, int32_t H, int32_t E,
                     int32_t K, float* logits, int32_t* topk_idx, float* topk_w, void* stream);
@@ -152,8 +152,12 @@ int moe_combine_residual_gate(const float* y_routed, const float* topk_w, const 
  *   x, residual: device float [H]; out: device float [H] (written; must not alias x,
  *   may alias residual); topk_idx/topk_w: device [K] (written).
  *   ws: device workspace of at least qmoe_workspace_bytes(L, 1) bytes, 256-byte
- *   aligned, ZERO-FILLED before its first use; each call leaves it zero-filled
- *   again on completion.  Calls that share a workspace must be stream-ordered.
+ *   aligned, ZERO-FILLED before its first use.  The library keeps state in it from
+ *   call to call (a call counter, a status word, values tagged with the call
+ *   number), so the caller must not write to it afterwards.  Calls that share a
+ *   workspace must be stream-ordered.  Word 1 (int32 at byte offset 4) is a status
+ *   word: nonzero if a bounded wait inside the kernel ran out (the output of that
+ *   call is then undefined); the caller may read it after the stream passes.
  */
 int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual, float* out,
                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
@@ -163,8 +167,9 @@ int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual
  * token t): tokens are grouped per routed expert (histogram, scan, stable scatter)
  * so each active expert's weights are read once per batch.
  *   x, residual, out: device float [T][H]; topk_idx/topk_w: device [T][K] (written).
- *   ws: at least qmoe_workspace_bytes(L, T) bytes, zero-filled before first use
- *   and left zero-filled.  1 <= T <= 256.
+ *   ws: at least qmoe_workspace_bytes(L, T) bytes, 256-byte aligned, zero-filled
+ *   before its first use (the same workspace may serve moe_layer_forward).
+ *   1 <= T <= 256.
  */
 int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* residual,
                               float* out, int32_t T, int32_t* topk_idx, float* topk_w, void* ws,

@@ -24,7 +24,7 @@ Value mappings (all exactly reproducible on both sides):
   halves; ``z = sum(halves) - 16 * 32767.5`` is an exact integer and
   ``v = f32(z) * f32(sigma / (65536 * sqrt(16/12)))``.  This is the
   Irwin-Hall sum of 16 uniforms: mean 0, standard deviation sigma, tails cut
-  at about 3.5 sigma * sqrt(3) -- a stand-in for the ~N(0, sigma) inputs;
+  at sqrt(48) sigma (about 6.9 sigma) -- a stand-in for the ~N(0, sigma) inputs;
 * bf16: round-to-nearest-even of the binary32 value, on the bit pattern.
 
 Canonical expert block (per expert, in this order): gate codes, up codes,
