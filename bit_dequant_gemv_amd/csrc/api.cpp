@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "qmoe_internal.h"
 
 namespace {
@@ -89,6 +91,20 @@ int check_qmat(const qmoe_qmat* W, int bits) {
 }  // namespace
 
 namespace qmoe {
+
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];  // zero-initialised; 0 = not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 qmoe_expert_offsets expert_offsets(int hidden, int inter, int bits) {
   qmoe_expert_offsets o;

@@ -4,6 +4,8 @@
 // "FMA 최적화 역양자화 커널" and "손으로 작성한 Metal 컴퓨트 셰이더".
 #include <math.h>
 
+#include <algorithm>
+
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -43,6 +45,8 @@ inline size_t prep_lds_bytes(int n) {
 
 // ---------------------------------------------------------------------------
 // y = W x
+// A persistent grid (a few workgroups per CU) walks the rows; each wave keeps the
+// next R rows' loads in flight while it reduces the current ones.
 // ---------------------------------------------------------------------------
 template <int BITS, int LG, int CPL, int R>
 __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ codes,
@@ -57,9 +61,8 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ co
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
   load_x_shared<BITS, LG, CPL>(rd, x, cols, C, gl);
-  const int64_t nw = (int64_t)gridDim.x * (kBlock / 64);
-  for (int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
-       base < rows; base += nw * RPW * R) {
+  const int64_t step = (int64_t)gridDim.x * (kBlock / 64) * RPW * R;
+  auto fetch_rows = [&](int64_t base, uint4 (&q)[R][CPL], uint32_t (&s)[R][CPL]) {
     const uint8_t* crow[R];
     const uint32_t* srow[R];
     bool ok[R];
@@ -67,28 +70,47 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ co
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r * RPW + sub;
       ok[r] = row < rows;
-      crow[r] = codes + row * rowbytes;
-      srow[r] = sb + row * G;
+      crow[r] = codes + (ok[r] ? row : 0) * rowbytes;
+      srow[r] = sb + (ok[r] ? row : 0) * G;
     }
-    uint4 q[R][CPL];
-    uint32_t s[R][CPL];
     rd.template fetch<R>(crow, srow, ok, C, gl, q, s);
+  };
+  int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
+  uint4 q[R][CPL];
+  uint32_t s[R][CPL];
+  if (base < rows) fetch_rows(base, q, s);
+  for (; base < rows; base += step) {
+    uint4 qn[R][CPL];
+    uint32_t sn[R][CPL];
+    if (base + step < rows) fetch_rows(base + step, qn, sn);
     float p[R];
     rd.template dots<R>(q, s, p);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v = group_sum<LG>(p[r]);
-      if (gl == 0 && ok[r]) y[base + r * RPW + sub] = v;
+      if (gl == 0 && base + r * RPW + sub < rows) y[base + r * RPW + sub] = v;
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        q[r][i] = qn[r][i];
+        s[r][i] = sn[r][i];
+      }
   }
 }
+
+// workgroups per CU for the persistent stand-alone GEMV (measured best: 4)
+constexpr int kQgemvBlocksPerCU = 4;
 
 template <int BITS, int LG, int CPL>
 hipError_t run_qgemv(const uint8_t* codes, const uint32_t* sb, const float* x, float* y, int rows,
                      int cols, hipStream_t s) {
   constexpr int R = RowsPerPass<CPL>::R;
   const int64_t waves = (rows + (64 / LG) * R - 1) / ((64 / LG) * R);
-  const int blocks = (int)(waves < 4 * 8192 ? ceil_div(waves, 4) : 8192);
+  const int cus = device_cus();
+  const int64_t cap = (int64_t)kQgemvBlocksPerCU * (cus > 0 ? cus : 256);
+  const int blocks = (int)std::min<int64_t>(ceil_div(waves, 4), cap);
   hipLaunchKernelGGL((k_qgemv<BITS, LG, CPL, R>), dim3(blocks), dim3(kBlock),
                      prep_lds_bytes<BITS>(cols), s, codes, sb, x, y, rows, cols);
   return hipGetLastError();

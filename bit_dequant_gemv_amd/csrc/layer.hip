@@ -113,15 +113,14 @@ __device__ void read_done_to_lds(const uint64_t* src, int n, uint32_t tag, float
   }
 }
 
-// 64-bit selection key: larger key = larger value, ties to the lower index.
-// Zero is below every key of a finite value.
-__device__ __forceinline__ uint64_t sort_key(float v, int e) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+// Order-preserving u32 key of a float's bits (larger key = larger value; -0 is
+// mapped to +0 first, so the two zeros tie).  Key 0 means "no expert": no finite
+// value maps to it.
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  b = b == 0x80000000u ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t k) {
-  const uint32_t o = (uint32_t)(k >> 32);
+__device__ __forceinline__ float key_value(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
@@ -142,14 +141,16 @@ __device__ __forceinline__ lds_void_ptr lds_ptr(T* p) {
   return (lds_void_ptr)(p);
 }
 
-// LDS DMA (global_load_lds): lane l's 16 (or 4) bytes land at lds + 16*l (4*l).
+// LDS DMA (global_load_lds): lane l's 16 (or 4) bytes land at lds + 16*l (4*l),
+// with the non-temporal cache policy (cache-policy bit 1) like every weight load.
 // Kept in plain device functions: calling the builtin directly inside the kernel
 // template makes the host-side kernel handle go missing.
+constexpr int kCpolNT = 2;
 __device__ __forceinline__ void dma16(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, kCpolNT);
 }
 __device__ __forceinline__ void dma4(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, kCpolNT);
 }
 
 template <int BITS, int H, int I>
@@ -186,17 +187,17 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   const int gli = lane % LGI, subi = lane / LGI;
   const int row0 = wg * kRB;
 
+  __shared__ __align__(16) float s_x[H];          // the layer input x
   __shared__ uint32_t s_xp[CH * PW];
   __shared__ float s_xsc[CH], s_xsum[CH];
   __shared__ float s_h[(kFusedMaxK + 1) * I];   // routed h (k < K), shared h (k = K)
   __shared__ float s_y[kFusedMaxK + 1][kRB];
   __shared__ float s_part[kLW];
-  __shared__ int s_idx[kFusedMaxK];
-  __shared__ float s_w[kFusedMaxK];
   __shared__ uint32_t s_tag;
   __shared__ float s_rv[kLW];
-  __shared__ uint64_t s_key[kFusedMaxE + 16 * kLW];
-  __shared__ uint64_t s_ck[kLW * kFusedMaxK];
+  __shared__ uint32_t s_wmax[kLW];             // top-K: largest key of each wave
+  __shared__ uint32_t s_ncand;                 // number of candidates
+  __shared__ uint64_t s_cand[kFusedMaxE + 8];  // candidates: key << 32 | expert (+ padding)
   __shared__ uint4 s_dq[kLW * kSlots * 64];     // down-row codes fetched by LDS DMA
   __shared__ uint32_t s_ds[kLW * kSlots * 64];  // their scale/bias words
   bool ok_all = true;
@@ -205,25 +206,27 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   if (threadIdx.x == 0)
     epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- 1. loads: router rows, one shared gate/up pair, shared down rows (DMA)
+  // ---- 1. loads: x (once per workgroup, into LDS below) and the shared-gate
+  //         vector, then the router rows, one shared gate/up pair and the shared
+  //         down rows (DMA).  x goes first: vector memory returns in order.
+  uint4 gq = make_uint4(0u, 0u, 0u, 0u);  // shared-gate vector chunk for gamma (step 8)
+  float gx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if ((int)threadIdx.x < H / 8) {
+    const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[0];
+    const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[1];
+    gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
+    gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
+    gq = reinterpret_cast<const uint4*>(A.g)[threadIdx.x];
+  }
   const int quarter = wv & 3;
   uint4 rq[CPLR];
-  float rx[CPLR][8];
   auto router_fetch = [&](int row) {
 #pragma unroll
     for (int i = 0; i < CPLR; ++i) {
       const int cq = lane + 64 * i;
-      const int c = quarter * CRQ + cq;
       const bool ok = row < E && cq < CRQ;
-      rq[i] = ok ? reinterpret_cast<const uint4*>(A.router + (int64_t)row * H)[c]
+      rq[i] = ok ? ld_stream16(A.router + (int64_t)row * H + 8 * (quarter * CRQ + cq))
                  : make_uint4(0u, 0u, 0u, 0u);
-      float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
-      if (ok) {
-        f0 = reinterpret_cast<const float4*>(A.x + 8 * c)[0];
-        f1 = reinterpret_cast<const float4*>(A.x + 8 * c)[1];
-      }
-      rx[i][0] = f0.x; rx[i][1] = f0.y; rx[i][2] = f0.z; rx[i][3] = f0.w;
-      rx[i][4] = f1.x; rx[i][5] = f1.y; rx[i][6] = f1.z; rx[i][7] = f1.w;
     }
   };
   router_fetch(wg * 2 + (wv >> 2));
@@ -251,15 +254,11 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
          lds_ptr(&s_ds[sl * 64]));
   }
   const float resid = (int)threadIdx.x < kRB ? A.residual[row0 + threadIdx.x] : 0.f;
-  uint4 gq = make_uint4(0u, 0u, 0u, 0u);  // shared-gate vector chunk for gamma (step 8)
-  float gx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if ((int)threadIdx.x < H / 8) {
-    gq = reinterpret_cast<const uint4*>(A.g)[threadIdx.x];
-    const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[0];
-    const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[1];
-    gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
-    gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
+    reinterpret_cast<float4*>(s_x)[2 * threadIdx.x] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+    reinterpret_cast<float4*>(s_x)[2 * threadIdx.x + 1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
   }
+  __syncthreads();
 
   // ---- 2. router dots -> logits (the writers, threads 0 and 1, are in the same
   //         wave as the epoch reader, so the tag needs no barrier)
@@ -270,7 +269,15 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     if (r0 != wg * 2) router_fetch(r0 + (wv >> 2));
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPLR; ++i) acc += bf16_chunk_dot(rq[i], rx[i]);
+    for (int i = 0; i < CPLR; ++i) {
+      const int cq = lane + 64 * i;
+      if (cq < CRQ) {
+        const float4* xp = reinterpret_cast<const float4*>(s_x) + 2 * (quarter * CRQ + cq);
+        const float4 f0 = xp[0], f1 = xp[1];
+        const float xr8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        acc += bf16_chunk_dot(rq[i], xr8);
+      }
+    }
     acc = group_sum<64>(acc);
     if (lane == 0) s_part[wv] = acc;
     __syncthreads();
@@ -282,10 +289,23 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   }
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
-  prep_x_coop<BITS>(A.x, H, s_xp, s_xsc, s_xsum, threadIdx.x, kLB);
-  if (threadIdx.x == 0) s_tag = tag0;
+  prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, threadIdx.x, kLB);
+  if (threadIdx.x == 0) {
+    s_tag = tag0;
+    s_ncand = 0;
+  }
   __syncthreads();
   const uint32_t tag = s_tag;
+
+  // First read of the logits (thread t holds experts t + j*kLB), issued now so
+  // that it is in flight during step 4.
+  uint64_t lraw[PER_L];
+#pragma unroll
+  for (int j = 0; j < PER_L; ++j) {
+    const int e = threadIdx.x + j * kLB;
+    lraw[j] = e < E ? tag_get(A.logits + e) : 0;
+  }
+  asm volatile("" ::: "memory");  // keep those loads issued here, ahead of step 4
 
   // ---- 4. shared gate/up + SwiGLU -> hs (stored after the top-K: nothing needs it
   //         before step 8, and a store now would be waited for by the logit poll)
@@ -301,22 +321,30 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     hs_val = silu_f(a) * u;
   }
 
-  // ---- 5. top-K by ranking 64-bit keys (order: larger value, then lower index)
+  // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the logits'
+  //         bits mapped to an order-preserving u32 (-0 counts as +0).
+  //         (a) the largest key of each wave; (b) L = the K-th largest of these 8 is
+  //         at most the K-th largest key overall (K waves hold a key >= L), so the
+  //         picks are among the keys >= L; (c) those candidates -- a handful for
+  //         spread-out logits, at most E -- are appended to an LDS list; (d) every
+  //         wave ranks them itself: each candidate counts those ahead of it (larger
+  //         key, or equal key and lower index), and rank r < K is the r-th pick,
+  //         read out with ballots.  Every wave ends with the same uniform answer.
+  int eidx[kFusedMaxK];
+  float elog[kFusedMaxK];
   {
-    float lv[PER_L];
+    uint32_t key[PER_L];
     uint32_t pending = 0;
 #pragma unroll
-    for (int j = 0; j < PER_L; ++j)
+    for (int j = 0; j < PER_L; ++j) {
+      key[j] = 0;
       if ((int)threadIdx.x + j * kLB < E) pending |= 1u << j;
-    for (uint32_t spins = 0; pending; ++spins) {
-      uint64_t v[PER_L];
+    }
+    for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
       for (int j = 0; j < PER_L; ++j)
-        v[j] = (pending >> j) & 1u ? tag_get(A.logits + threadIdx.x + j * kLB) : 0;
-#pragma unroll
-      for (int j = 0; j < PER_L; ++j)
-        if (((pending >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
-          lv[j] = __uint_as_float((uint32_t)v[j]);
+        if (((pending >> j) & 1u) && (uint32_t)(lraw[j] >> 32) == tag) {
+          key[j] = order_key((uint32_t)lraw[j]);
           pending &= ~(1u << j);
         }
       if (!pending) break;
@@ -325,77 +353,87 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-    }
-    // Wave w owns the block of keys [w*EB, w*EB + EB) (EB a multiple of 16; the
-    // padding is zero and never wins).  Each lane counts the keys of its block
-    // that beat its own; the K best of every block are candidates, and wave 0
-    // ranks the 8K candidates the same way.  Rank r < K is the r-th expert.
-    const int EB = ((E + kLW - 1) / kLW + 15) & ~15;
 #pragma unroll
-    for (int j = 0; j < PER_L; ++j) {
-      const int e = threadIdx.x + j * kLB;
-      if (e < E) s_key[e] = sort_key(lv[j], e);
+      for (int j = 0; j < PER_L; ++j)
+        if ((pending >> j) & 1u) lraw[j] = tag_get(A.logits + threadIdx.x + j * kLB);
     }
-    for (int q = E + threadIdx.x; q < kLW * EB; q += kLB) s_key[q] = 0;
-    if (threadIdx.x < kLW * kFusedMaxK) s_ck[threadIdx.x] = 0;
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int j = 0; j < PER_L; ++j) lmax = max(lmax, key[j]);
+    const uint32_t wmax = wave_max_u32(lmax);
+    if (lane == 0) s_wmax[wv] = wmax;
     __syncthreads();
-    const int b0 = wv * EB;
-    const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(s_key + b0);
-    for (int e = b0 + lane; e < b0 + EB; e += 64) {
-      const uint64_t key = s_key[e];
-      int r0 = 0, r1 = 0;
-#pragma unroll 8
-      for (int q = 0; q < EB / 2; ++q) {  // broadcast reads: every lane reads the same words
-        const ulonglong2 kk = kb[q];
-        r0 += kk.x > key ? 1 : 0;
-        r1 += kk.y > key ? 1 : 0;
+    uint32_t L;
+    {
+      const uint32_t mi = lane < kLW ? s_wmax[lane] : 0u;
+      int n = 0;  // how many wave maxima are >= mine
+#pragma unroll
+      for (int w = 0; w < kLW; ++w) n += (uint32_t)__builtin_amdgcn_readlane((int)mi, w) >= mi ? 1 : 0;
+      L = wave_max_u32(lane < kLW && n >= K ? mi : 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < PER_L; ++j)
+      if (key[j] != 0 && key[j] >= L) {
+        const uint32_t slot = atomicAdd(&s_ncand, 1u);
+        s_cand[slot] = ((uint64_t)key[j] << 32) | (uint32_t)(threadIdx.x + j * kLB);
       }
-      const int rk = r0 + r1;
-      if (key != 0 && rk < K) s_ck[wv * kFusedMaxK + rk] = key;
-    }
     __syncthreads();
-    if (wv == 0) {
-      const uint64_t key = lane < kLW * kFusedMaxK ? s_ck[lane] : 0;
+    const int nc = (int)s_ncand;
+#pragma unroll
+    for (int r = 0; r < kFusedMaxK; ++r) {
+      eidx[r] = -1;
+      elog[r] = 0.f;
+    }
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const bool have = c0 + lane < nc;
+      const uint64_t cv = have ? s_cand[c0 + lane] : 0;
+      const uint64_t me = (cv & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)cv);
       int rk = 0;
-      const ulonglong2* cb = reinterpret_cast<const ulonglong2*>(s_ck);
+      for (int c = 0; c < nc; c += 8) {
+        // eight broadcast reads in flight (the list is padded, so no read is
+        // conditional; entries at or past nc are ignored)
+        uint64_t o[8];
 #pragma unroll
-      for (int q = 0; q < kLW * kFusedMaxK / 2; ++q) {
-        const ulonglong2 kk = cb[q];
-        rk += (kk.x > key ? 1 : 0) + (kk.y > key ? 1 : 0);
+        for (int u = 0; u < 8; ++u) o[u] = s_cand[c + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          rk += (c + u < nc &&
+                 ((o[u] & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)o[u])) > me)
+                    ? 1
+                    : 0;
       }
-      if (key != 0 && rk < K) {
-        s_idx[rk] = (int)(0xFFFFFFFFu - (uint32_t)key);
-        s_w[rk] = key_value(key);  // logit for now
-      }
-      // thread 0 belongs to wave 0: no barrier between the ranks and the softmax
-      if (lane == 0) {
-        const float m = s_w[0];
-        float ex[kFusedMaxK];
-        float sum = 0.f;
 #pragma unroll
-        for (int k = 0; k < kFusedMaxK; ++k) {
-          ex[k] = k < K ? __expf(s_w[k] - m) : 0.f;
-          sum += ex[k];
-        }
-        const float inv = 1.0f / sum;
-#pragma unroll
-        for (int k = 0; k < kFusedMaxK; ++k)
-          if (k < K) s_w[k] = ex[k] * inv;
-        if (wg == 0) {
-#pragma unroll
-          for (int k = 0; k < kFusedMaxK; ++k)
-            if (k < K) {
-              A.idx_out[k] = s_idx[k];
-              A.w_out[k] = s_w[k];
-            }
+      for (int r = 0; r < kFusedMaxK; ++r) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(have && rk == r && r < K);
+        if (m) {
+          const int wl = __builtin_ctzll(m);
+          eidx[r] = __builtin_amdgcn_readlane((int)(uint32_t)cv, wl);
+          elog[r] = key_value((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), wl));
         }
       }
     }
-    __syncthreads();
   }
-  int eidx[kFusedMaxK];
+  // renormalised softmax over the K picks (uniform values)
+  float wsel[kFusedMaxK];
+  {
+    float sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < kFusedMaxK; ++k) eidx[k] = k < K ? s_idx[k] : -1;
+    for (int k = 0; k < kFusedMaxK; ++k) {
+      wsel[k] = k < K ? __expf(elog[k] - elog[0]) : 0.f;
+      sum += wsel[k];
+    }
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int k = 0; k < kFusedMaxK; ++k) wsel[k] *= inv;
+  }
+  if (wg == 0 && threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < kFusedMaxK; ++k)
+      if (k < K) {
+        A.idx_out[k] = eidx[k];
+        A.w_out[k] = wsel[k];
+      }
+  }
   if (has_sp && glh == 0) tag_put(hs + jsp, hs_val, tag);
 
   // ---- 6. loads: two routed gate/up row pairs per wave, then the routed down rows
@@ -520,7 +558,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 #pragma unroll
     for (int w = 0; w < kLW; ++w) gs += s_rv[w];
     float acc = resid;
-    for (int k = 0; k < K; ++k) acc = fmaf(s_w[k], s_y[k][threadIdx.x], acc);
+#pragma unroll
+    for (int k = 0; k < kFusedMaxK; ++k)
+      if (k < K) acc = fmaf(wsel[k], s_y[k][threadIdx.x], acc);
     A.out[row0 + threadIdx.x] = fmaf(sigmoid_f(gs), s_y[kFusedMaxK][threadIdx.x], acc);
   }
   if (!ok_all) flag_status(A.ctrl, 1u);
@@ -590,22 +630,15 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return c;
-  static int cus[64] = {0};  // per-device CU count; concurrent first calls store equal values
-  if (dev < 0 || dev >= 64) return c;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return c;
-    cus[dev] = n;
-  }
+  const int cus = device_cus();
+  if (cus <= 0) return c;
   int blocks_per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, reinterpret_cast<const void*>(fn),
                                                    kLB, 0) != hipSuccess ||
       blocks_per_cu < 1)
     return c;
   const int nb = H / kRB;
-  if (nb > cus[dev] * blocks_per_cu) return c;  // every workgroup must be resident at once
+  if (nb > cus * blocks_per_cu) return c;  // every workgroup must be resident at once
   const int bits = L.routed.bits;
   const int ch = H * bits / 128;
   const int rpwh = 64 / (ch >= 64 ? 64 : ch);

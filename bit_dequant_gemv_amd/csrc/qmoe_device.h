@@ -82,6 +82,35 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each half row
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Largest / smallest u32 over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -340,6 +369,19 @@ struct RowDotF {
   }
 };
 
+// Streaming loads of weights: non-temporal (the nt cache policy), so a stream that
+// is read once does not displace reused lines from the caches.  On gfx950 this
+// also raises the sustained read rate of a long weight stream (measured: 4.8 ->
+// 6.2 TB/s for a 288 MB 4-bit matrix).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // A lane's slice of x (as fixed-point planes) for one matrix, and the row dots.
 template <int BITS, int LG, int CPL>
 struct RowDot {
@@ -430,8 +472,8 @@ struct RowDot {
       for (int i = 0; i < CPL; ++i) {
         const int c = gl + i * LG;
         if (ok[r] && c < C) {
-          q[r][i] = *reinterpret_cast<const uint4*>(crow[r] + 16 * c);
-          s[r][i] = srow[r][c / QTraits<BITS>::CPG];
+          q[r][i] = ld_stream16(crow[r] + 16 * c);
+          s[r][i] = ld_stream4(srow[r] + c / QTraits<BITS>::CPG);
         } else {
           q[r][i] = make_uint4(0u, 0u, 0u, 0u);
           s[r][i] = 0u;

@@ -44,6 +44,9 @@ hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float
                                 float* out, int T, int32_t* idx, float* w, void* ws,
                                 hipStream_t s);
 
+// compute units of the current device (cached per device); 0 if it cannot be read
+int device_cus();
+
 // offsets of the canonical expert block
 qmoe_expert_offsets expert_offsets(int hidden, int inter, int bits);
 
