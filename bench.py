@@ -1,19 +1,27 @@
-"""Benchmark of the batch-1 quantized MoE layer on one MI355X.
+"""Benchmark of the batch-1 quantized MoE hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
 
-A step is one token through one MoE layer (config 1/2: 512 resident 4-bit or
-2-bit experts of 4096x1024 plus a shared expert, router GEMV, top-4, SwiGLU,
-combine), one token through the 60-layer stack (config 3), one 64-token batch
-(config 4) or one expert FFN call (config 0).  Inputs are synthetic (seeded
-Philox streams generated in HBM); weights and activations are resident in HBM
-before the timed region starts.  Steps are enqueued as replays of HIP graphs of
-consecutive launches, so the host never synchronises inside the timed region.
+Workloads (all weights 4-bit unless noted; H = 4096, I = 1024, group 64):
+  --config 1 (default)  one MoE layer at batch 1: router over 512 resident experts,
+                        top-4 + shared expert, SwiGLU, combine; a step is one token
+  --config 2            the same layer with 2-bit experts
+  --config 0            one expert FFN call (gate, up, SwiGLU, down) on an expert
+                        picked from 256 resident ones; a step is one call
+  --config 3            a 60-layer stack (218 GB resident), RMSNorm before each
+                        layer; a step is one token through all 60 layers
+  --config 4            batched decode of 64 tokens through the config-1 layer;
+                        a step is one batch
+Inputs are synthetic (seeded Philox streams generated in HBM); weights and
+activations are resident in HBM before the timed region starts.  Steps are
+enqueued as replays of HIP graphs, so the host never synchronises inside the
+timed region.
 
 Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one launch
-of the dominant kernel divided by its average launch duration over the timed
-region (HIP events on the launch stream); `cpu_baseline` times the float64
-oracle on a bounded sample of the same workload on the host cores.
+of the dominant kernel (for configs 0 and 4: of one call, all its kernels) divided
+by its average duration over the timed region (HIP events on the launch stream);
+`cpu_baseline` times the float64 oracle on a bounded sample of the same workload
+on the host cores.
 """
 from __future__ import annotations
 
@@ -256,12 +264,187 @@ def run_copy(torch):
     return 2 * 4 * n / dt / 1e9
 
 
+def timed_steps(torch, calls, steps, warmup, per_graph):
+    """Capture calls (one per step, cycled) into graphs of per_graph steps and time
+    exactly `steps` of them.  Returns seconds."""
+    per_graph = max(1, min(per_graph, len(calls)))
+    n = (len(calls) // per_graph) * per_graph
+    graphs = capture_graphs(torch, calls[:n], per_graph)
+    tail = None
+    if steps % per_graph:
+        tail = capture_graphs(torch, calls[:steps % per_graph], per_graph)[0]
+    warm = (max(0, warmup) + per_graph - 1) // per_graph
+    return time_graphs(torch, graphs, steps // per_graph, warm, tail)
+
+
+def run_ffn_bench(args, torch, q, synth):
+    """One expert FFN per step on an expert drawn from 256 resident ones (1.8 GB)."""
+    seed, n_exp = 1000, 256
+    pool = q.ExpertPool.allocate(n_exp, H, I, 4)
+    synth.fill_expert_pool(pool.buf, pool.stride, n_exp, 0, 0, seed, H, I, 4)
+    n_ring = 1024
+    X = make_x_ring(torch, synth, seed, n_ring)
+    # a fixed pseudo-random walk over the experts (every expert visited, no repeats in a row)
+    order = torch.tensor([(t * 97 + 13) % n_exp for t in range(n_ring)], dtype=torch.int32, device="cuda")
+    Y = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, q.qmoe_ffn_workspace_bytes(pool, 1)), dtype=torch.uint8, device="cuda")
+    calls = [(lambda t=t: q.expert_ffn_swiglu(pool, order[t:t + 1], X[t], Y.view(1, H), ws))
+             for t in range(n_ring)]
+    steps = max(1, args.steps)
+    dt = timed_steps(torch, calls, steps, args.warmup, 256)
+    per_call = expert_bytes(4) + 2 * H * 4
+    launch_s = dt / steps
+    roof = {"bound": "hbm", "achieved": round(per_call / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(per_call / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles("expert_ffn_w4")}
+    extra = {"kernel": "expert_ffn_swiglu (k_ffn_gateup + k_ffn_down), roofline over the whole call",
+             "bytes_per_call": per_call, "avg_call_us": round(launch_s * 1e6, 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_ffn(seed, n_exp, args.cpu_seconds)
+    return {"value": steps / dt, "unit": "expert FFN calls/s", "steps": steps, "dt": dt, "roof": roof,
+            "extra": extra, "cpu": cpu, "workload": "expert_ffn_batch1_4bit", "bits": 4,
+            "cfg": {"experts_resident": n_exp}}
+
+
+def cpu_oracle_ffn(seed, n_exp, target_s):
+    import oracle
+    import synth
+    blocks = [synth.expert_block(seed, 0, e, H, I, 4) for e in range(4)]
+    xs = [synth.activations(seed, t, H) for t in range(8)]
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s and done < 4096:
+        oracle.expert_ffn(blocks[done % 4], xs[done % 8], H, I, 4)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "expert FFN calls/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} calls on 4 experts (float64 numpy oracle, host-resident inputs)"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def run_stack_bench(args, torch, q, synth):
+    """60 layers of the config-1 layer, RMSNorm before each; 256 sequential tokens."""
+    seed, n_layers, n_tok = 1003, 60, 256
+    layers = [LayerWorkload(seed, l, 4, torch, q, synth) for l in range(n_layers)]
+    norm = []
+    for l in range(n_layers):
+        w = torch.empty(H, dtype=torch.float32, device="cuda")
+        synth.fill_uniform_f32(w, seed, synth.tensor_id(synth.K_NORM_W, 0, l), synth.NORM_LO, synth.NORM_HI)
+        norm.append(w)
+    H0 = make_x_ring(torch, synth, seed, n_tok)
+    h = torch.empty(H, dtype=torch.float32, device="cuda")
+    xb = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+
+    def token(t):
+        h.copy_(H0[t])
+        for l in range(n_layers):
+            q.rmsnorm_f32(h, norm[l], 1e-6, xb)
+            q.moe_layer_forward(layers[l].L, xb, h, h, idx, w, layers[l].ws)
+
+    calls = [(lambda t=t: token(t)) for t in range(n_tok)]
+    steps = max(1, min(args.steps, 4096))
+    dt = timed_steps(torch, calls, steps, args.warmup, 8)
+    for W in layers[:1]:
+        if int(W.ws[4:8].view(torch.int32).item()) != 0:
+            raise RuntimeError("fused layer kernel reported a time-out")
+    per_tok = n_layers * (layer_bytes(4) + 2 * H * 4)
+    tok_s = steps / dt
+    roof = {"bound": "hbm", "achieved": round(per_tok * tok_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": None}
+    extra = {"kernel": "k_layer x60 + k_rmsnorm x60 per token (roofline over the token)",
+             "bytes_per_token": per_tok, "layer_evals_per_s": round(tok_s * n_layers, 1),
+             "resident_GB": round(sum(W.routed.buf.numel() + W.shared.buf.numel() for W in layers) / 1e9, 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_stack(seed, n_layers, args.cpu_seconds)
+    return {"value": tok_s, "unit": "tokens/s (60-layer stack)", "steps": steps, "dt": dt, "roof": roof,
+            "extra": extra, "cpu": cpu, "workload": "moe_stack60_batch1_4bit", "bits": 4,
+            "cfg": {"layers": n_layers, "tokens": n_tok, "rmsnorm_eps": 1e-6}}
+
+
+def cpu_oracle_stack(seed, n_layers, target_s):
+    """Oracle layers of one token through the stack, as many as fit in target_s;
+    extrapolated to the 60 layers of a token."""
+    import numpy as np
+
+    import oracle
+    import synth
+    h = synth.activations(seed, 0, H).astype(np.float64)
+    done, spent, wall0 = 0, 0.0, time.perf_counter()
+    for l in range(n_layers):
+        if done and time.perf_counter() - wall0 > 3 * target_s:  # input generation counts here
+            break
+        R = synth.router(seed, l, E, H)
+        g = synth.shared_gate(seed, l, H)
+        shared = synth.expert_block(seed, l, E, H, I, 4)
+        nw = synth.norm_weight(seed, l, H)
+        x = oracle.rmsnorm(h, nw, 1e-6)
+        idx, _ = oracle.router_topk(oracle.router_logits(R, x), K)
+        blocks = {int(e): synth.expert_block(seed, l, int(e), H, I, 4) for e in idx}
+        t0 = time.perf_counter()
+        x = oracle.rmsnorm(h, nw, 1e-6)
+        h = oracle.moe_layer(blocks.__getitem__, shared, R, g, x, h, H, I, 4, K)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent > target_s:
+            break
+    per_layer = spent / done
+    return {"value": 1.0 / (per_layer * n_layers), "unit": "tokens/s (60-layer stack)",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} layers of one token (float64 numpy oracle, host-resident inputs), "
+                      f"extrapolated to {n_layers} layers"}
+
+
+def run_batched_bench(args, torch, q, synth):
+    """64 tokens per step through the config-1 layer, grouped per expert."""
+    seed, T = 1004, 64
+    W = LayerWorkload(seed, 0, 4, torch, q, synth)
+    n_ring = 64
+    X = make_x_ring(torch, synth, seed, n_ring * T).view(n_ring, T, H)
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    ws = q.alloc_workspace(W.L, T)
+    calls = [(lambda b=b: q.moe_layer_forward_batched(W.L, X[b], X[b], out, idx, w, ws)) for b in range(n_ring)]
+    steps = max(1, min(args.steps, 8192))
+    dt = timed_steps(torch, calls, steps, args.warmup, 64)
+    # distinct experts per batch, averaged over the ring (read back after timing)
+    distinct = []
+    for b in range(n_ring):
+        q.moe_layer_forward_batched(W.L, X[b], X[b], out, idx, w, ws)
+        distinct.append(len(set(idx.cpu().numpy().ravel().tolist())))
+    d_avg = sum(distinct) / len(distinct)
+    per_batch = E * H * 2 + (d_avg + 1) * expert_bytes(4) + H * 2 + 3 * T * H * 4
+    batch_s = dt / steps
+    roof = {"bound": "hbm", "achieved": round(per_batch / batch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(per_batch / batch_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None}
+    extra = {"kernel": "moe_layer_forward_batched (router, grouping, grouped gate/up, down, combine), "
+                       "roofline over the whole call", "distinct_experts_avg": round(d_avg, 1),
+             "bytes_per_batch": int(per_batch), "avg_batch_us": round(batch_s * 1e6, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_layer(seed, 0, 4, list(range(64)), args.cpu_seconds)
+    return {"value": steps * T / dt, "unit": "tokens/s", "steps": steps, "dt": dt, "roof": roof,
+            "extra": extra, "cpu": cpu, "workload": f"moe_layer_batched{T}_4bit", "bits": 4,
+            "cfg": {"batch": T}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16384)
     ap.add_argument("--warmup", type=int, default=1024)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -274,25 +457,39 @@ def main():
     import bit_dequant_gemv_amd as q
     import synth
     torch.cuda.set_device(0)
-    bits = 4 if args.config == 1 else 2
-    tok_s, steps, dt, roof, extra, (seed, bits) = run_layer_bench(args, torch, q, synth, bits)
-    gbps, us = run_qgemv_stream(torch, q, synth)
-    extra["qgemv_w4_131072x4096_GBps"] = round(gbps, 1)
-    extra["qgemv_w4_131072x4096_frac_of_peak"] = round(gbps / HBM_PEAK_GBPS, 4)
-    extra["qgemv_w4_131072x4096_avg_launch_us"] = round(us, 2)
-    extra["copy_1GiB_GBps"] = round(run_copy(torch), 1)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_oracle_layer(seed, 0, bits, list(range(64)), args.cpu_seconds)
+    extra0 = {}
+    if args.config in (1, 2):
+        # stand-alone GEMV stream and copy reference first, on an otherwise empty device
+        gbps, us = run_qgemv_stream(torch, q, synth)
+        extra0["qgemv_w4_131072x4096_GBps"] = round(gbps, 1)
+        extra0["qgemv_w4_131072x4096_frac_of_peak"] = round(gbps / HBM_PEAK_GBPS, 4)
+        extra0["qgemv_w4_131072x4096_avg_launch_us"] = round(us, 2)
+        extra0["copy_1GiB_GBps"] = round(run_copy(torch), 1)
+        torch.cuda.empty_cache()
+        bits = 4 if args.config == 1 else 2
+        tok_s, steps, dt, roof, extra, (seed, _) = run_layer_bench(args, torch, q, synth, bits)
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_oracle_layer(seed, 0, bits, list(range(64)), args.cpu_seconds)
+        r = {"value": tok_s, "unit": "tokens/s", "steps": steps, "dt": dt, "roof": roof, "extra": extra,
+             "cpu": cpu, "workload": f"moe_layer_batch1_{bits}bit", "bits": bits, "cfg": {}}
+    elif args.config == 0:
+        r = run_ffn_bench(args, torch, q, synth)
+    elif args.config == 3:
+        r = run_stack_bench(args, torch, q, synth)
+    else:
+        r = run_batched_bench(args, torch, q, synth)
+    r["extra"].update(extra0)
+    config = {"workload": r["workload"], "experts": E, "hidden": H, "inter": I, "top_k": K,
+              "shared_experts": 1, "group": 64, "bits": r["bits"]}
+    config.update(r["cfg"])
+    config["device"] = torch.cuda.get_device_name(0)
     line = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / steps, 6),
+        "metric": METRIC, "value": round(r["value"], 1), "unit": r["unit"], "n_gpus": 1,
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["dt"] * 1e3 / r["steps"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"moe_layer_batch1_{bits}bit", "experts": E, "hidden": H, "inter": I,
-                   "top_k": K, "shared_experts": 1, "group": 64, "bits": bits,
-                   "device": torch.cuda.get_device_name(0)},
-        "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+        "data": "synthetic", "config": config,
+        "roofline": r["roof"], "cpu_baseline": r["cpu"], "detail": r["extra"],
     }
     print(json.dumps(line), flush=True)
 

@@ -135,24 +135,6 @@ __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) 
   return a0 + a1;
 }
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-template <typename T>
-__device__ __forceinline__ lds_void_ptr lds_ptr(T* p) {
-  return (lds_void_ptr)(p);
-}
-
-// LDS DMA (global_load_lds): lane l's 16 (or 4) bytes land at lds + 16*l (4*l),
-// with the non-temporal cache policy (cache-policy bit 1) like every weight load.
-// Kept in plain device functions: calling the builtin directly inside the kernel
-// template makes the host-side kernel handle go missing.
-constexpr int kCpolNT = 2;
-__device__ __forceinline__ void dma16(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, kCpolNT);
-}
-__device__ __forceinline__ void dma4(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, kCpolNT);
-}
-
 template <int BITS, int H, int I>
 __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // ---- compile-time geometry
