@@ -67,6 +67,8 @@ _SIGS = {
     "moe_combine_residual_gate": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_layer_forward": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
+    "moe_layer_forward_norm": ([ctypes.POINTER(LayerC), _vp, _vp, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
+                               ctypes.c_int),
     "moe_layer_forward_batched": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
                                    _vp], ctypes.c_int),
     "qmoe_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
@@ -248,6 +250,23 @@ def moe_layer_forward(layer: Layer, x, residual=None, out=None, idx=None, w=None
                                   _ptr(residual, torch.float32, "residual"), _ptr(out, torch.float32, "out"),
                                   _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
                                   _ptr(ws, None, "ws"), ws.numel(), _stream()), "moe_layer_forward")
+    return out, idx, w
+
+
+def moe_layer_forward_norm(layer: Layer, h, norm_w, eps=1e-6, out=None, idx=None, w=None, ws=None):
+    """One fused launch of h + MoE(rmsnorm(h)): returns (out [H], idx int32 [K], w [K]).
+    out may be h itself (an in-place step of the residual stream)."""
+    dev = h.device
+    out = out if out is not None else torch.empty_like(h)
+    idx = idx if idx is not None else torch.empty(layer.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(layer.top_k, dtype=torch.float32, device=dev)
+    if ws is None:
+        raise ValueError("pass a persistent workspace from alloc_workspace(layer)")
+    _check(_lib.moe_layer_forward_norm(ctypes.byref(layer.c()), _ptr(h, torch.float32, "h"),
+                                       _ptr(norm_w, torch.float32, "norm_w"), eps,
+                                       _ptr(out, torch.float32, "out"), _ptr(idx, torch.int32, "idx"),
+                                       _ptr(w, torch.float32, "w"), _ptr(ws, None, "ws"), ws.numel(),
+                                       _stream()), "moe_layer_forward_norm")
     return out, idx, w
 
 

@@ -223,9 +223,26 @@ int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual
   const size_t need = qmoe_workspace_bytes(L, 1);
   if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
   if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
-  return hip_status(qmoe::launch_layer(*L, x, residual, out, topk_idx, topk_w, ws,
+  return hip_status(qmoe::launch_layer(*L, x, nullptr, 0.f, residual, out, topk_idx, topk_w, ws,
                                        static_cast<hipStream_t>(stream)),
                     "moe_layer_forward launch");
+}
+
+int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* norm_w, float eps,
+                           float* out, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_vec(h, "h"))) return rc;
+  if ((rc = check_vec(norm_w, "norm_w"))) return rc;
+  if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");
+  if (!out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  const size_t need = qmoe_workspace_bytes(L, 1);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  return hip_status(qmoe::launch_layer(*L, h, norm_w, eps, h, out, topk_idx, topk_w, ws,
+                                       static_cast<hipStream_t>(stream)),
+                    "moe_layer_forward_norm launch");
 }
 
 int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* residual,

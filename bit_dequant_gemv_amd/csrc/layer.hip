@@ -64,7 +64,9 @@ struct LayerArgs {
   int64_t off_g, off_u, off_d, off_gsb, off_usb, off_dsb;
   const uint16_t* router;
   const uint16_t* g;
-  const float* x;
+  const float* x;         // the layer input, or (norm_w set) the stream h it is normalised from
+  const float* norm_w;    // RMSNorm weight [H], or null
+  float eps;
   const float* residual;
   float* out;
   int32_t* idx_out;
@@ -236,6 +238,29 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
          lds_ptr(&s_ds[sl * 64]));
   }
   const float resid = (int)threadIdx.x < kRB ? A.residual[row0 + threadIdx.x] : 0.f;
+  if (A.norm_w) {
+    // RMSNorm of the input stream, computed by every workgroup: x = h / sqrt(mean(h^2) + eps) * w
+    float nw[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    if ((int)threadIdx.x < H / 8) {
+      const float4 w0 = reinterpret_cast<const float4*>(A.norm_w + 8 * threadIdx.x)[0];
+      const float4 w1 = reinterpret_cast<const float4*>(A.norm_w + 8 * threadIdx.x)[1];
+      nw[0] = w0.x; nw[1] = w0.y; nw[2] = w0.z; nw[3] = w0.w;
+      nw[4] = w1.x; nw[5] = w1.y; nw[6] = w1.z; nw[7] = w1.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(gx[i], gx[i], ss);
+    }
+    ss = group_sum<64>(ss);
+    if (lane == 0) s_part[wv] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) tot += s_part[w];
+    const float r = 1.0f / sqrtf(tot / (float)H + A.eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gx[i] = gx[i] * r * nw[i];
+    __syncthreads();  // s_part is reused by the router dots
+  }
   if ((int)threadIdx.x < H / 8) {
     reinterpret_cast<float4*>(s_x)[2 * threadIdx.x] = make_float4(gx[0], gx[1], gx[2], gx[3]);
     reinterpret_cast<float4*>(s_x)[2 * threadIdx.x + 1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
@@ -570,8 +595,9 @@ WsLayout fused_ws(int E, int H, int I) {
 }
 
 // unfused fallback: logits[E] | y_routed[K][H] | y_shared[H] | h[K][I] (ctrl block stays zero)
+// | xn[H] (the normalised input, for the RMSNorm variant)
 struct UnfusedWs {
-  int64_t logits, yr, ys, h, total;
+  int64_t logits, yr, ys, h, xn, total;
 };
 
 UnfusedWs unfused_ws(int E, int K, int H, int I) {
@@ -580,7 +606,8 @@ UnfusedWs unfused_ws(int E, int K, int H, int I) {
   u.yr = u.logits + align256((int64_t)E * 4);
   u.ys = u.yr + align256((int64_t)K * H * 4);
   u.h = u.ys + align256((int64_t)H * 4);
-  u.total = u.h + align256((int64_t)K * I * 4);
+  u.xn = u.h + align256((int64_t)K * I * 4);
+  u.total = u.xn + align256((int64_t)H * 4);
   return u;
 }
 
@@ -647,8 +674,9 @@ size_t layer_workspace_bytes(const qmoe_layer& L) {
   return (size_t)(f.total > u.total ? f.total : u.total);
 }
 
-hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residual, float* out,
-                        int32_t* idx, float* w, void* ws, hipStream_t s) {
+hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w, float eps,
+                        const float* residual, float* out, int32_t* idx, float* w, void* ws,
+                        hipStream_t s) {
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   KernelFn fn = fused_kernel(L);
@@ -669,6 +697,8 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residu
     A.router = L.router;
     A.g = L.shared_gate;
     A.x = x;
+    A.norm_w = norm_w;
+    A.eps = eps;
     A.residual = residual;
     A.out = out;
     A.idx_out = idx;
@@ -690,7 +720,13 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residu
   float* ys = reinterpret_cast<float*>(wsb + u.ys);
   float* h = reinterpret_cast<float*>(wsb + u.h);
   const int32_t* zero_idx = reinterpret_cast<const int32_t*>(wsb) + CTRL_ZERO;  // stays zero
-  hipError_t err = launch_router_topk(L.router, x, 1, H, E, K, logits, idx, w, s);
+  hipError_t err = hipSuccess;
+  if (norm_w) {
+    float* xn = reinterpret_cast<float*>(wsb + u.xn);
+    err = launch_rmsnorm(x, norm_w, eps, H, xn, s);
+    x = xn;
+  }
+  if (err == hipSuccess) err = launch_router_topk(L.router, x, 1, H, E, K, logits, idx, w, s);
   if (err == hipSuccess) err = launch_ffn(L.routed, idx, K, x, 0, yr, h, s);
   if (err == hipSuccess) err = launch_ffn(L.shared, zero_idx, 1, x, 0, ys, h, s);
   if (err == hipSuccess) err = launch_combine(yr, w, ys, L.shared_gate, x, residual, out, H, K, s);

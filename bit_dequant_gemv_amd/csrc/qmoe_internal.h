@@ -35,8 +35,10 @@ hipError_t launch_rmsnorm(const float* v, const float* w, float eps, int n, floa
 
 // fused single-launch layer (layer.hip)
 size_t layer_workspace_bytes(const qmoe_layer& L);
-hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* residual, float* out,
-                        int32_t* idx, float* w, void* ws, hipStream_t s);
+// norm_w null: x is the layer input; else the input is rmsnorm(x) with weight norm_w
+hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w, float eps,
+                        const float* residual, float* out, int32_t* idx, float* w, void* ws,
+                        hipStream_t s);
 
 // batched decode (batched.hip)
 size_t batched_workspace_bytes(const qmoe_layer& L, int T);

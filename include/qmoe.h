@@ -163,6 +163,20 @@ int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual
                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same layer with its input RMS-normalised inside the launch: a decoder
+ * stack step h <- h + MoE(rmsnorm(h)) ([PK] Metal shaders: two-stage RMS
+ * normalisation; "지연 GPU 전문가 실행 (Deferred CMD3)": the normalised combine
+ * output feeds the next layer).  x = h / sqrt(mean(h^2) + eps) * norm_w,
+ * residual = h.
+ *   h: device float [H] (the residual stream); norm_w: device float [H];
+ *   out: device float [H] (written; may alias h); topk_idx/topk_w as above;
+ *   ws: as for moe_layer_forward (the same workspace may serve both).
+ */
+int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* norm_w, float eps,
+                           float* out, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * Batched decode of T tokens through one layer (row t equals moe_layer_forward on
  * token t): tokens are grouped per routed expert (histogram, scan, stable scatter)
  * so each active expert's weights are read once per batch.

@@ -319,6 +319,52 @@ def test_layer_output_may_alias_residual(q):
     _check_layer_token(D, x, rr.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), residual=r)
 
 
+@pytest.mark.parametrize("E,H,I,bits,K", [(512, 4096, 1024, 4, 4), (64, 1024, 256, 2, 4),
+                                          (16, 192, 128, 4, 2)])
+def test_layer_norm_variant(q, E, H, I, bits, K):
+    """h <- h + MoE(rmsnorm(h)) in one launch (fused shapes) or through the fallback
+    chain (the last shape): against the oracle, and against rmsnorm_f32 followed by
+    moe_layer_forward; out written in place over h."""
+    say("layer norm variant", E, H, I, bits, K)
+    D = DeviceLayer(6000 + E + bits, 3, E, H, I, bits, K)
+    ws = q.alloc_workspace(D.L)
+    nw = synth.norm_weight(D.seed, 3, H)
+    dnw = torch.from_numpy(nw).cuda()
+    for tok in range(2):
+        h0 = host_x(D.seed, 20 + tok, H)
+        h = torch.from_numpy(h0).cuda()
+        # the two-call chain on a copy
+        xn = q.rmsnorm_f32(h.clone(), dnw, 1e-6)
+        ref_out, ref_idx, _ = q.moe_layer_forward(D.L, xn, h.clone(), ws=ws)
+        out, idx, w = q.moe_layer_forward_norm(D.L, h, dnw, 1e-6, out=h, ws=ws)
+        torch.cuda.synchronize()
+        assert _status(ws) == 0
+        assert out.data_ptr() == h.data_ptr()
+        xr = oracle.rmsnorm(h0, nw, 1e-6)
+        _check_layer_token(D, xr, h.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), residual=h0)
+        if torch.equal(idx, ref_idx):
+            r = _rel(h.cpu().numpy(), ref_out.cpu().numpy().astype(np.float64))
+            say("  norm variant vs chain rel_l2", r)
+            assert r <= 1e-5
+
+
+def test_layer_call_counter_wraps(q):
+    """The call tag in the workspace wraps past 2^32 - 1 without being mistaken for
+    a zero-filled word."""
+    say("call counter wrap")
+    D = DeviceLayer(4001, 0, 64, 1024, 256, 4, 4)
+    ws = q.alloc_workspace(D.L)
+    ws[0:4].view(torch.int32).fill_(-2)  # counter = 0xFFFFFFFE
+    x = host_x(D.seed, 3, 1024)
+    for t in range(3):
+        out, idx, w = q.moe_layer_forward(D.L, torch.from_numpy(x).cuda(), ws=ws)
+        torch.cuda.synchronize()
+        assert _status(ws) == 0
+        _check_layer_token(D, x, out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy())
+    # 0xFFFFFFFE -> 0xFFFFFFFF -> 1 (0 skipped) -> 2
+    assert _epoch(ws) == 2
+
+
 # ---------------------------------------------------------------------------
 # batched decode (tokens grouped per expert)
 # ---------------------------------------------------------------------------
@@ -369,10 +415,9 @@ def test_stack_parity(q):
         h = torch.from_numpy(h0).cuda()
         gpu_idx = []
         for l, D in enumerate(layers):
-            x = q.rmsnorm_f32(h, dnorm[l], 1e-6)
-            out, idx, _ = q.moe_layer_forward(D.L, x, h, ws=ws[l])
+            # one launch per layer, in place: h <- h + MoE(rmsnorm(h))
+            _, idx, _ = q.moe_layer_forward_norm(D.L, h, dnorm[l], 1e-6, out=h, ws=ws[l])
             gpu_idx.append(idx.cpu().numpy())
-            h = out
         torch.cuda.synchronize()
         # oracle end to end; a near-tie is resolved the way the GPU did after checking validity
         hr = h0.astype(np.float64)
