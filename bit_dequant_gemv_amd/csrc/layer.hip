@@ -174,7 +174,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __shared__ __align__(16) float s_x[H];          // the layer input x
   __shared__ uint32_t s_xp[CH * PW];
   __shared__ float s_xsc[CH], s_xsum[CH];
-  __shared__ float s_h[(kFusedMaxK + 1) * I];   // routed h (k < K), shared h (k = K)
+  __shared__ __align__(16) float s_h[(kFusedMaxK + 1) * I];  // routed h (k < K), shared h (k = K)
+  __shared__ __align__(16) uint32_t s_hp[(kFusedMaxK + 1) * CI * PW];  // their planes
+  __shared__ float s_hsc[(kFusedMaxK + 1) * CI], s_hsum[(kFusedMaxK + 1) * CI];
   __shared__ float s_y[kFusedMaxK + 1][kRB];
   __shared__ float s_part[kLW];
   __shared__ uint32_t s_tag;
@@ -182,6 +184,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __shared__ uint32_t s_wmax[kLW];             // top-K: largest key of each wave
   __shared__ uint32_t s_ncand;                 // number of candidates
   __shared__ uint64_t s_cand[kFusedMaxE + 8];  // candidates: key << 32 | expert (+ padding)
+  __shared__ uint64_t s_pick[kFusedMaxK];      // the picks, in rank order
   __shared__ uint4 s_dq[kLW * kSlots * 64];     // down-row codes fetched by LDS DMA
   __shared__ uint32_t s_ds[kLW * kSlots * 64];  // their scale/bias words
   bool ok_all = true;
@@ -304,22 +307,13 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __syncthreads();
   const uint32_t tag = s_tag;
 
-  // First read of the logits (thread t holds experts t + j*kLB), issued now so
-  // that it is in flight during step 4.
-  uint64_t lraw[PER_L];
-#pragma unroll
-  for (int j = 0; j < PER_L; ++j) {
-    const int e = threadIdx.x + j * kLB;
-    lraw[j] = e < E ? tag_get(A.logits + e) : 0;
-  }
-  asm volatile("" ::: "memory");  // keep those loads issued here, ahead of step 4
-
-  // ---- 4. shared gate/up + SwiGLU -> hs (stored after the top-K: nothing needs it
-  //         before step 8, and a store now would be waited for by the logit poll)
   uint64_t* hs = A.hs + (size_t)(tag % kSlotsH) * I;
   uint64_t* hr = A.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
   dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
   float hs_val = 0.f;
+  // ---- 4. shared gate/up + SwiGLU -> hs (one item per wave at most; the logits
+  //         of the other workgroups are still on their way meanwhile; hs is stored
+  //         after the top-K)
   if (has_sp) {
     float p[2];
     dH.template dots<2>(qsp, ssp, p);
@@ -328,24 +322,29 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     hs_val = silu_f(a) * u;
   }
 
-  // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the logits'
-  //         bits mapped to an order-preserving u32 (-0 counts as +0).
-  //         (a) the largest key of each wave; (b) L = the K-th largest of these 8 is
-  //         at most the K-th largest key overall (K waves hold a key >= L), so the
-  //         picks are among the keys >= L; (c) those candidates -- a handful for
-  //         spread-out logits, at most E -- are appended to an LDS list; (d) every
-  //         wave ranks them itself: each candidate counts those ahead of it (larger
-  //         key, or equal key and lower index), and rank r < K is the r-th pick,
-  //         read out with ballots.  Every wave ends with the same uniform answer.
-  int eidx[kFusedMaxK];
-  float elog[kFusedMaxK];
+  // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the
+  //         logits' bits mapped to an order-preserving u32 (-0 counts as +0).
+  //         (a) every thread polls its logits; the largest key of each wave;
+  //         (b) L = the K-th largest of these 8 is at most the K-th largest key
+  //             overall (K waves hold a key >= L), so the picks are among the keys
+  //             >= L; those candidates -- a handful for spread-out logits, at most
+  //             E -- are appended to an LDS list;
+  //         (c) the last wave ranks them: each candidate counts those ahead of it
+  //             (larger key, or equal key and lower index), rank r < K is the r-th
+  //             pick; the picks go to the other waves through LDS.
   {
+    uint64_t lraw[PER_L];
     uint32_t key[PER_L];
     uint32_t pending = 0;
 #pragma unroll
     for (int j = 0; j < PER_L; ++j) {
+      const int e = threadIdx.x + j * kLB;
       key[j] = 0;
-      if ((int)threadIdx.x + j * kLB < E) pending |= 1u << j;
+      lraw[j] = 0;
+      if (e < E) {
+        pending |= 1u << j;
+        lraw[j] = tag_get(A.logits + e);
+      }
     }
     for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
@@ -385,40 +384,51 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
         s_cand[slot] = ((uint64_t)key[j] << 32) | (uint32_t)(threadIdx.x + j * kLB);
       }
     __syncthreads();
+  }
+  if (wv == kLW - 1) {
     const int nc = (int)s_ncand;
+    uint64_t pick[kFusedMaxK];  // key << 32 | expert; expert 0xFFFFFFFF = none
 #pragma unroll
-    for (int r = 0; r < kFusedMaxK; ++r) {
-      eidx[r] = -1;
-      elog[r] = 0.f;
-    }
+    for (int r = 0; r < kFusedMaxK; ++r) pick[r] = 0xFFFFFFFFull;
+    // pad the list to a multiple of 8 with zero keys: a zero key is never ahead
+    if (lane < 8) s_cand[nc + lane] = 0;
     for (int c0 = 0; c0 < nc; c0 += 64) {
       const bool have = c0 + lane < nc;
       const uint64_t cv = have ? s_cand[c0 + lane] : 0;
       const uint64_t me = (cv & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)cv);
       int rk = 0;
-      for (int c = 0; c < nc; c += 8) {
-        // eight broadcast reads in flight (the list is padded, so no read is
-        // conditional; entries at or past nc are ignored)
+      for (int c = 0; c < nc; c += 8) {  // eight broadcast reads in flight
         uint64_t o[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) o[u] = s_cand[c + u];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          rk += (c + u < nc &&
-                 ((o[u] & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)o[u])) > me)
-                    ? 1
-                    : 0;
+          rk += ((o[u] & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)o[u])) > me ? 1 : 0;
       }
 #pragma unroll
       for (int r = 0; r < kFusedMaxK; ++r) {
         const uint64_t m = __builtin_amdgcn_ballot_w64(have && rk == r && r < K);
         if (m) {
           const int wl = __builtin_ctzll(m);
-          eidx[r] = __builtin_amdgcn_readlane((int)(uint32_t)cv, wl);
-          elog[r] = key_value((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), wl));
+          pick[r] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), wl) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv, wl);
         }
       }
     }
+    if (lane < kFusedMaxK) {
+#pragma unroll
+      for (int r = 0; r < kFusedMaxK; ++r)
+        if (lane == r) s_pick[r] = pick[r];
+    }
+  }
+  __syncthreads();
+  int eidx[kFusedMaxK];
+  float elog[kFusedMaxK];
+#pragma unroll
+  for (int r = 0; r < kFusedMaxK; ++r) {
+    const uint64_t v = r < K ? s_pick[r] : 0xFFFFFFFFull;
+    eidx[r] = (int)(uint32_t)v;
+    elog[r] = key_value((uint32_t)(v >> 32));
   }
   // renormalised softmax over the K picks (uniform values)
   float wsel[kFusedMaxK];
@@ -533,15 +543,27 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB>(hr, K * I, tag, s_h);
   read_done_to_lds<(I + kLB - 1) / kLB>(hs, I, tag, s_h + kFusedMaxK * I);
   __syncthreads();
+  // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
+  // two vectors; unused routed slots hold stale values whose planes are not read)
+  prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, threadIdx.x, kLB);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 6) has landed
+  __syncthreads();
   const float gpart = group_sum<64>(bf16_chunk_dot(gq, gx));
   if (lane == 0) s_rv[wv] = gpart;
-  RowDotF<BITS, LGI> dF;
+  RowDot<BITS, LGI, 1> dD;
+  auto load_h = [&](int k) {
+    dD.load_prepped(s_hp + k * CI * PW, s_hsc + k * CI, s_hsum + k * CI, CI, gli);
+  };
+  auto down_row = [&](int sl, bool ok) {
+    const uint4 qd[1][1] = {{ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u)}};
+    const uint32_t sd[1][1] = {{ok ? s_ds[sl * 64 + lane] : 0u}};
+    float p[1];
+    dD.template dots<1>(qd, sd, p);
+    return group_sum<LGI>(p[0]);
+  };
   if (wv < DITEMS) {
-    dF.load_x(s_h + kFusedMaxK * I, CI, gli);
-    const int sl = wv * kSlots;
-    const float v = group_sum<LGI>(dF.dot(sd_ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u),
-                                          sd_ok ? s_ds[sl * 64 + lane] : 0u));
+    load_h(kFusedMaxK);
+    const float v = down_row(wv * kSlots, sd_ok);
     if (gli == 0 && nl_s < kRB) s_y[kFusedMaxK][nl_s] = v;
   }
 #pragma unroll
@@ -549,11 +571,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     const int t = wv * MAXR + m;
     if (t < K * DITEMS) {
       const int k = t / DITEMS, d = t % DITEMS;
-      if (m == 0 || d == 0) dF.load_x(s_h + k * I, CI, gli);  // a new expert for this wave
-      const bool ok = (slot_ok >> (1 + m)) & 1u;
-      const int sl = wv * kSlots + 1 + m;
-      const float v = group_sum<LGI>(dF.dot(ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u),
-                                            ok ? s_ds[sl * 64 + lane] : 0u));
+      if (m == 0 || d == 0) load_h(k);  // a new expert for this wave
+      const float v = down_row(wv * kSlots + 1 + m, (slot_ok >> (1 + m)) & 1u);
       const int nl = d * RPWI + subi;
       const bool eok_k = (unsigned)eidx[k < kFusedMaxK ? k : 0] < (unsigned)E;
       if (gli == 0 && nl < kRB) s_y[k][nl] = eok_k ? v : __builtin_nanf("");

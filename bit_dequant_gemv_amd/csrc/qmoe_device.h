@@ -154,6 +154,32 @@ __device__ __forceinline__ uint32_t to_u24(float x, float f) {
   return (uint32_t)((int)rintf(x * f) + (1 << 23));
 }
 
+// Nibble transpose of eight 24-bit values: out[d] holds digit d (bits 4d..4d+3) of
+// e[j] in nibble j, d = 0..5.  Byte permutes gather byte b of the even and of the
+// odd elements (one byte per element), then masks split each gathered byte into
+// its low digit (2b) and high digit (2b+1), already in element order.
+__device__ __forceinline__ void nibble_planes8(const uint32_t (&e)[8], uint32_t* out) {
+  constexpr uint32_t M = 0x0F0F0F0Fu;
+  uint32_t E[3], O[3];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t a = e[par], b = e[2 + par], c = e[4 + par], d = e[6 + par];
+    const uint32_t x01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a.B0 b.B0 a.B1 b.B1
+    const uint32_t y01 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c.B0 d.B0 c.B1 d.B1
+    const uint32_t x2 = __builtin_amdgcn_perm(b, a, 0x0C0C0602u);   // a.B2 b.B2 0 0
+    const uint32_t y2 = __builtin_amdgcn_perm(d, c, 0x0C0C0602u);   // c.B2 d.B2 0 0
+    uint32_t* g = par ? O : E;
+    g[0] = __builtin_amdgcn_perm(y01, x01, 0x05040100u);  // byte 0 of a, b, c, d
+    g[1] = __builtin_amdgcn_perm(y01, x01, 0x07060302u);  // byte 1
+    g[2] = __builtin_amdgcn_perm(y2, x2, 0x05040100u);    // byte 2
+  }
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    out[2 * b] = (E[b] & M) | ((O[b] & M) << 4);
+    out[2 * b + 1] = ((E[b] >> 4) & M) | (O[b] & ~M);
+  }
+}
+
 // Planes of one 32-bit code word worth of x values (v: EPW values, f from chunk_exp).
 // 4-bit: out[d], d = 0..5, nibble j = digit d of element j.
 // 2-bit: out[h*6 + d]: half h = 0 pairs with (w & 0x33333333) << 2 (elements
@@ -166,26 +192,16 @@ __device__ __forceinline__ void prep_word(const float* v, float f, uint32_t* out
 #pragma unroll
   for (int j = 0; j < EPW; ++j) u[j] = to_u24(v[j], f);
   if (BITS == 4) {
-#pragma unroll
-    for (int d = 0; d < 6; ++d) {
-      uint32_t p = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p |= ((u[j] >> (4 * d)) & 15u) << (4 * j);
-      out[d] = p;
-    }
+    const uint32_t e[8] = {u[0], u[1], u[2], u[3], u[4], u[5], u[6], u[7]};
+    nibble_planes8(e, out);
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      // nibble k of half h holds element 2k + h of the word
+      uint32_t e[8];
 #pragma unroll
-      for (int d = 0; d < 6; ++d) {
-        uint32_t p = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          p |= ((u[4 * b + h] >> (4 * d)) & 15u) << (8 * b);
-          p |= ((u[4 * b + 2 + h] >> (4 * d)) & 15u) << (8 * b + 4);
-        }
-        out[h * 6 + d] = p;
-      }
+      for (int k = 0; k < 8; ++k) e[k] = u[(2 * k + h) % EPW];
+      nibble_planes8(e, out + 6 * h);
     }
   }
 }
