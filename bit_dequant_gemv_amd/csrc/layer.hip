@@ -88,6 +88,10 @@ __device__ __forceinline__ uint64_t tag_get(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima; gfx9 field layout)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -453,8 +457,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   }
   if (has_sp && glh == 0) tag_put(hs + jsp, hs_val, tag);
 
-  // ---- 6. loads: two routed gate/up row pairs per wave, then the routed down rows
-  //         of this workgroup's output rows (LDS DMA, slots 1..MAXR)
+  // ---- 6. loads: two routed gate/up row pairs per wave
   const int n_rp = K * NSP;
   int it = rank;
   uint4 q[4][CPLH];
@@ -486,25 +489,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     dH.template fetch<4>(cr, sr, ok, CH, glh, q, sq);
   };
   if (it < n_rp) fetch_pairs(it);
-  uint32_t slot_ok = sd_ok ? 1u : 0u;
-#pragma unroll
-  for (int m = 0; m < MAXR; ++m) {
-    const int t = wv * MAXR + m;
-    const int k = t / DITEMS, d = t % DITEMS;
-    const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
-    const int nl = d * RPWI + subi;
-    const bool ok = (unsigned)e < (unsigned)E && nl < kRB && row0 + nl < H;
-    if (ok) {
-      const uint8_t* blk = A.rbase + (int64_t)e * A.rstride;
-      const int sl = wv * kSlots + 1 + m;
-      dma16(blk + A.off_d + (row0 + nl) * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
-      dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (row0 + nl) * GI +
-               gli / QTraits<BITS>::CPG,
-           lds_ptr(&s_ds[sl * 64]));
-      slot_ok |= 2u << m;
-    }
-  }
-
   // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step
   for (; it < n_rp; it += 2 * W) {
     if (it != rank) fetch_pairs(it);
@@ -518,9 +502,33 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
         tag_put(hr + kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
     }
   }
-  // completion: every store of this workgroup acknowledged, then one tagged flag
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // ---- 7b. the routed down rows of this workgroup's output rows (LDS DMA, slots
+  //          1..MAXR), issued only now: they are needed after the h hand-off, not
+  //          before it, so they stay out of the way of the gate/up rows.  Every
+  //          wave issues exactly 2*MAXR DMA instructions (an unused slot reads a
+  //          valid row it then ignores), so the wait below can leave them in flight.
+  uint32_t slot_ok = sd_ok ? 1u : 0u;
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) {
+    const int t = wv * MAXR + m;
+    const int k = t / DITEMS, d = t % DITEMS;
+    const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
+    const int nl = d * RPWI + subi;
+    const bool ok = (unsigned)e < (unsigned)E && nl < kRB && row0 + nl < H;
+    const uint8_t* blk = ok ? A.rbase + (int64_t)e * A.rstride : A.sblk;
+    const int rowd = ok ? row0 + nl : 0;
+    const int sl = wv * kSlots + 1 + m;
+    dma16(blk + A.off_d + rowd * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
+    dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + rowd * GI + gli / QTraits<BITS>::CPG,
+         lds_ptr(&s_ds[sl * 64]));
+    if (ok) slot_ok |= 2u << m;
+  }
+  // completion: every store of this workgroup acknowledged (all vector memory
+  // operations but the 2*MAXR DMA just issued), then one tagged flag
+  // (a bare barrier: it only orders the acknowledged stores of every wave before
+  // the flag; no LDS is handed over here, and a fence would wait for the DMA)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * MAXR));
+  __builtin_amdgcn_s_barrier();
   if (threadIdx.x == 0) tag_put(A.flags + wg, 0.f, tag);
 
   // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
