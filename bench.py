@@ -56,11 +56,17 @@ def layer_bytes(bits: int) -> int:
 
 
 def sources_sha() -> str:
+    """Hash of the kernel sources' code: comment-only lines and blank lines are
+    left out, so editing a comment does not invalidate counters taken on the
+    same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_dequant_gemv_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            for line in open(os.path.join(csrc, f), encoding="utf-8"):
+                t = line.strip()
+                if t and not t.startswith("//"):
+                    h.update(t.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -10,21 +10,23 @@
 // NB = H/16 workgroups of 8 waves; workgroup b owns output rows [16b, 16b+16).
 // "rank" = wave * NB + workgroup numbers the waves so that consecutive ranks sit
 // in different workgroups.  Schedule of a workgroup:
-//   1. issue loads: its router rows (4 waves per row), one shared-expert gate/up
-//      row pair per rank below I/RPWH, and (by LDS DMA) its shared-expert down rows;
+//   1. issue loads: x (staged in LDS; RMS-normalised here when the layer is given
+//      a norm weight), the shared-gate vector, its router rows (4 waves per row),
+//      one shared-expert gate/up row pair per rank below I/RPWH, and (by LDS DMA)
+//      its shared-expert down rows;
 //   2. router dots -> logits (tagged stores);
 //   3. x as fixed-point planes in LDS (once per workgroup);
-//   4. shared gate/up + SwiGLU -> hs (tagged);
-//   5. wait for the E logits; top-K by ranking 64-bit keys (ties to the lower
-//      index); renormalised softmax of the K selected logits;
-//   6. issue loads: the routed down rows of its output rows (LDS DMA), the
-//      shared-gate vector g, and two routed gate/up row pairs per wave;
-//   7. routed gate/up dots + SwiGLU -> hr (tagged);
-//   8. wait for every workgroup's completion flag; read hr and hs; gamma =
+//   4. shared gate/up + SwiGLU -> hs (while the other logits are in flight);
+//   5. top-K: every thread polls its logits; from the 8 wave maxima a lower bound
+//      L of the K-th largest logit; the keys >= L go to an LDS list; one wave
+//      ranks them (larger value, then lower index) and passes the picks on;
+//      renormalised softmax of the K selected logits;
+//   6. issue loads: two routed gate/up row pairs per wave;
+//   7. routed gate/up dots + SwiGLU -> hr (tagged); then the routed down rows of
+//      this workgroup (LDS DMA), a wait for everything else, one tagged flag;
+//   8. wait for every workgroup's flag; read hr and hs; their planes; gamma =
 //      sigmoid(g . x); shared and routed down rows; out = residual +
 //      sum_k w_k y_k + gamma y_shared.
-// (Anything waited for after step 6's loads waits for them too: vector memory
-// results return in order.  So nothing between steps 6 and 7 waits on memory.)
 // Values that cross workgroups (logits, hs, hr) are 64-bit words (epoch << 32 |
 // value bits) written with agent-scope atomic stores (write-through to the
 // device coherence point), so they never need resetting.  The logits are polled
