@@ -193,8 +193,10 @@ __global__ __launch_bounds__(kBB) void k_bgateup(PoolArgsB P, GroupTables G,
                                                  const uint32_t* __restrict__ xp,
                                                  float* __restrict__ h, int rows_per_block) {
   constexpr int RPW = 64 / LG;
-  const int gi = blockIdx.y;
-  if (gi >= G.n_groups[0]) return;
+  // groups in reverse: the shared expert's chunks (the most tokens each) start first
+  const int ng = G.n_groups[0];
+  if ((int)blockIdx.y >= ng) return;
+  const int gi = ng - 1 - (int)blockIdx.y;
   const int e = G.group_expert[gi];
   const bool eok = e == -1 || (unsigned)e < (unsigned)P.E;
   const uint8_t* blk = e == -1 ? P.sblk : P.rbase + (eok ? (int64_t)e * P.rstride : 0);
@@ -245,8 +247,10 @@ __global__ __launch_bounds__(kBB) void k_bdown(PoolArgsB P, GroupTables G,
                                                const uint32_t* __restrict__ hp,
                                                float* __restrict__ y, int rows_per_block) {
   constexpr int RPW = 64 / LG;
-  const int gi = blockIdx.y;
-  if (gi >= G.n_groups[0]) return;
+  // groups in reverse: the shared expert's chunks (the most tokens each) start first
+  const int ng = G.n_groups[0];
+  if ((int)blockIdx.y >= ng) return;
+  const int gi = ng - 1 - (int)blockIdx.y;
   const int e = G.group_expert[gi];
   const bool eok = e == -1 || (unsigned)e < (unsigned)P.E;
   const uint8_t* blk = e == -1 ? P.sblk : P.rbase + (eok ? (int64_t)e * P.rstride : 0);
