@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   constexpr int LGH = CH >= 64 ? 64 : CH;       // lanes per gate/up row
   constexpr int CPLH = CH / LGH;                // chunks per lane
   constexpr int RPWH = 64 / LGH;                // gate/up rows per wave pass
+  static_assert(LGH * CPLH == CH, "every chunk of a gate/up row has a lane");
   constexpr int GH = H / kGroup;
   constexpr int64_t RBH = (int64_t)H * BITS / 8;
   constexpr int CI = I * BITS / 128;            // 16-byte chunks per down row
@@ -169,7 +170,10 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   constexpr int kSlots = 1 + MAXR;
 
   const int NB = gridDim.x, wg = blockIdx.x;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform values go through readfirstlane so that their arithmetic (item,
+  // expert and row selection, load addresses) runs on the scalar unit
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int rank = wv * NB + wg;
   const int W = NB * kLW;
   const int E = A.E, K = A.K;
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     s_ncand = 0;
   }
   __syncthreads();
-  const uint32_t tag = s_tag;
+  const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_tag);
 
   uint64_t* hs = A.hs + (size_t)(tag % kSlotsH) * I;
   uint64_t* hr = A.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
@@ -433,8 +437,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 #pragma unroll
   for (int r = 0; r < kFusedMaxK; ++r) {
     const uint64_t v = r < K ? s_pick[r] : 0xFFFFFFFFull;
-    eidx[r] = (int)(uint32_t)v;
-    elog[r] = key_value((uint32_t)(v >> 32));
+    eidx[r] = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    elog[r] = key_value((uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)));
   }
   // renormalised softmax over the K picks (uniform values)
   float wsel[kFusedMaxK];
@@ -469,7 +473,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   auto fetch_pairs = [&](int it0) {
     const uint8_t* cr[4];
     const uint32_t* sr[4];
-    bool ok[4];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int item = it0 + v * W;
@@ -486,9 +489,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
       cr[2 * v + 1] = blk + A.off_u + jj[v] * RBH;
       sr[2 * v] = reinterpret_cast<const uint32_t*>(blk + A.off_gsb) + jj[v] * GH;
       sr[2 * v + 1] = reinterpret_cast<const uint32_t*>(blk + A.off_usb) + jj[v] * GH;
-      ok[2 * v] = ok[2 * v + 1] = eok[v];
     }
-    dH.template fetch<4>(cr, sr, ok, CH, glh, q, sq);
+    // unconditional: a row of a missing expert reads block 0 and is stored as NaN
+    dH.template fetch_always<4>(cr, sr, glh, q, sq);
   };
   if (it < n_rp) fetch_pairs(it);
   // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step

@@ -505,13 +505,31 @@ struct RowDot {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = gl + i * LG;
-        if (ok[r] && c < C) {
-          q[r][i] = ld_stream16(crow[r] + 16 * c);
-          s[r][i] = ld_stream4(srow[r] + c / QTraits<BITS>::CPG);
+        if (ok[r] && c < C) {  // unsigned lane offsets: a scalar row base plus a 32-bit offset
+          q[r][i] = ld_stream16(crow[r] + 16u * (uint32_t)c);
+          s[r][i] = ld_stream4(srow[r] + (uint32_t)c / QTraits<BITS>::CPG);
         } else {
           q[r][i] = make_uint4(0u, 0u, 0u, 0u);
           s[r][i] = 0u;
         }
+      }
+    }
+  }
+
+  // The same loads without per-row conditions: every row pointer is valid and
+  // every chunk gl + i*LG is < C (the caller guarantees both).  A straight run
+  // of loads lets each row's dots wait only for that row's data.
+  template <int R>
+  __device__ __forceinline__ void fetch_always(const uint8_t* const* crow,
+                                               const uint32_t* const* srow, int gl,
+                                               uint4 (&q)[R][CPL], uint32_t (&s)[R][CPL]) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t c = (uint32_t)(gl + i * LG);
+        q[r][i] = ld_stream16(crow[r] + 16u * c);
+        s[r][i] = ld_stream4(srow[r] + c / QTraits<BITS>::CPG);
       }
     }
   }
