@@ -298,8 +298,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
         acc += bf16_chunk_dot(rq[i], xr8);
       }
     }
-    acc = group_sum<64>(acc);
-    if (lane == 0) s_part[wv] = acc;
+    acc = group_sum_last<64>(acc);
+    if (lane == 63) s_part[wv] = acc;
     __syncthreads();
     if (threadIdx.x < 2 && r0 + (int)threadIdx.x < E) {
       const float* pp = s_part + 4 * threadIdx.x;
@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   if (has_sp) {
     float p[2];
     dH.template dots<2>(qsp, ssp, p);
-    const float a = group_sum<LGH>(p[0]);
-    const float u = group_sum<LGH>(p[1]);
+    const float a = group_sum_last<LGH>(p[0]);
+    const float u = group_sum_last<LGH>(p[1]);
     hs_val = silu_f(a) * u;
   }
 
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
         A.w_out[k] = wsel[k];
       }
   }
-  if (has_sp && glh == 0) tag_put(hs + jsp, hs_val, tag);
+  if (has_sp && group_last<LGH>(lane)) tag_put(hs + jsp, hs_val, tag);
 
   // ---- 6. loads: two routed gate/up row pairs per wave
   const int n_rp = K * NSP;
@@ -501,9 +501,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     dH.template dots<4>(q, sq, p);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const float a = group_sum<LGH>(p[2 * v]);
-      const float u = group_sum<LGH>(p[2 * v + 1]);
-      if (glh == 0 && it + v * W < n_rp)
+      const float a = group_sum_last<LGH>(p[2 * v]);
+      const float u = group_sum_last<LGH>(p[2 * v + 1]);
+      if (group_last<LGH>(lane) && it + v * W < n_rp)
         tag_put(hr + kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
     }
   }
@@ -512,7 +512,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   //          before it, so they stay out of the way of the gate/up rows.  Every
   //          wave issues exactly 2*MAXR DMA instructions (an unused slot reads a
   //          valid row it then ignores), so the wait below can leave them in flight.
-  uint32_t slot_ok = sd_ok ? 1u : 0u;
 #pragma unroll
   for (int m = 0; m < MAXR; ++m) {
     const int t = wv * MAXR + m;
@@ -526,7 +525,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     dma16(blk + A.off_d + rowd * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
     dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + rowd * GI + gli / QTraits<BITS>::CPG,
          lds_ptr(&s_ds[sl * 64]));
-    if (ok) slot_ok |= 2u << m;
   }
   // completion: every store of this workgroup acknowledged (all vector memory
   // operations but the 2*MAXR DMA just issued), then one tagged flag
@@ -561,34 +559,49 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, threadIdx.x, kLB);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 6) has landed
   __syncthreads();
-  const float gpart = group_sum<64>(bf16_chunk_dot(gq, gx));
-  if (lane == 0) s_rv[wv] = gpart;
-  RowDot<BITS, LGI, 1> dD;
-  auto load_h = [&](int k) {
-    dD.load_prepped(s_hp + k * CI * PW, s_hsc + k * CI, s_hsum + k * CI, CI, gli);
-  };
-  auto down_row = [&](int sl, bool ok) {
-    const uint4 qd[1][1] = {{ok ? s_dq[sl * 64 + lane] : make_uint4(0u, 0u, 0u, 0u)}};
-    const uint32_t sd[1][1] = {{ok ? s_ds[sl * 64 + lane] : 0u}};
-    float p[1];
-    dD.template dots<1>(qd, sd, p);
-    return group_sum<LGI>(p[0]);
-  };
-  if (wv < DITEMS) {
-    load_h(kFusedMaxK);
-    const float v = down_row(wv * kSlots, sd_ok);
-    if (gli == 0 && nl_s < kRB) s_y[kFusedMaxK][nl_s] = v;
-  }
+  const float gpart = group_sum_last<64>(bf16_chunk_dot(gq, gx));
+  if (lane == 63) s_rv[wv] = gpart;
+  // down rows: the wave's shared item (waves below DITEMS) and its MAXR routed
+  // items, which all belong to one expert kw, as one branch-free block so that
+  // their LDS reads, dots and reductions interleave; a slot without a row holds
+  // codes that are read and then ignored
+  static_assert(DITEMS % MAXR == 0, "the routed down items of a wave share one expert");
+  const int kw = (wv * MAXR) / DITEMS;
+  if (wv < DITEMS || kw < K) {
+    const int kr = kw < kFusedMaxK ? kw : kFusedMaxK;
+    RowDot<BITS, LGI, 1> dS, dR;
+    dS.load_prepped(s_hp + kFusedMaxK * CI * PW, s_hsc + kFusedMaxK * CI, s_hsum + kFusedMaxK * CI,
+                    CI, gli);
+    dR.load_prepped(s_hp + kr * CI * PW, s_hsc + kr * CI, s_hsum + kr * CI, CI, gli);
+    const uint4 qs[1][1] = {{s_dq[wv * kSlots * 64 + lane]}};
+    const uint32_t ss[1][1] = {{s_ds[wv * kSlots * 64 + lane]}};
+    uint4 qr[MAXR][1];
+    uint32_t sr[MAXR][1];
 #pragma unroll
-  for (int m = 0; m < MAXR; ++m) {
-    const int t = wv * MAXR + m;
-    if (t < K * DITEMS) {
-      const int k = t / DITEMS, d = t % DITEMS;
-      if (m == 0 || d == 0) load_h(k);  // a new expert for this wave
-      const float v = down_row(wv * kSlots + 1 + m, (slot_ok >> (1 + m)) & 1u);
-      const int nl = d * RPWI + subi;
-      const bool eok_k = (unsigned)eidx[k < kFusedMaxK ? k : 0] < (unsigned)E;
-      if (gli == 0 && nl < kRB) s_y[k][nl] = eok_k ? v : __builtin_nanf("");
+    for (int m = 0; m < MAXR; ++m) {
+      qr[m][0] = s_dq[(wv * kSlots + 1 + m) * 64 + lane];
+      sr[m][0] = s_ds[(wv * kSlots + 1 + m) * 64 + lane];
+    }
+    float ps[1], pr[MAXR];
+    dS.template dots<1>(qs, ss, ps);
+    dR.template dots<MAXR>(qr, sr, pr);
+    // every reduction before any (lane-masked) store, so that the rows overlap
+    const float vs = group_sum_last<LGI>(ps[0]);
+    float vr[MAXR];
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) vr[m] = group_sum_last<LGI>(pr[m]);
+    int ew = -1;
+#pragma unroll
+    for (int k = 0; k < kFusedMaxK; ++k)
+      if (k == kw) ew = eidx[k];
+    const bool eok_w = (unsigned)ew < (unsigned)E;
+    if (group_last<LGI>(lane)) {
+      if (wv < DITEMS && nl_s < kRB) s_y[kFusedMaxK][nl_s] = vs;
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m) {
+        const int nl = ((wv * MAXR + m) % DITEMS) * RPWI + subi;
+        if (kw < K && nl < kRB) s_y[kw][nl] = eok_w ? vr[m] : __builtin_nanf("");
+      }
     }
   }
   __syncthreads();

@@ -133,6 +133,31 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// The same sum, valid in the group's last lane (and, for LG <= 16, in every lane
+// of the group).  For LG = 32 and 64 the gfx9 DPP row broadcasts carry the row
+// sums on (lane 15 of a row into the next row; lane 31 into rows 2 and 3), so no
+// value leaves the vector unit.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int LG>
+__device__ __forceinline__ float group_sum_last(float v) {
+  if (LG >= 2) v += dpp_f<kDppXor1>(v);
+  if (LG >= 4) v += dpp_f<kDppXor2>(v);
+  if (LG >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (LG >= 16) v += dpp_f<kDppMirror>(v);
+  if (LG >= 32)  // rows 1 and 3 += the last lane of rows 0 and 2
+    v += __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+  if (LG >= 64)  // row 3 += lane 31
+    v += __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0x8, 0xF, false));
+  return v;
+}
+template <int LG>
+__device__ __forceinline__ bool group_last(int lane) {
+  return (lane & (LG - 1)) == LG - 1;
+}
+
 // Fixed-point parameters of a chunk with largest magnitude m: f = 2^(22-E) and
 // scale = 2^(E-22) where 2^E > m.  A zero (or negligibly small, < 2^-105) chunk
 // gets f = scale = 0; a chunk holding Inf/NaN gets scale = NaN.
