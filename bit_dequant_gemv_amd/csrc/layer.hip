@@ -98,25 +98,30 @@ __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Read n tagged values after their producers have all signalled completion: an
-// ordinary (L2-cacheable) load, so the 32 workgroups of an XCD share one fetch
-// from memory; a word still carrying an old tag comes from a stale cached line
-// (the buffer slot was last used several calls ago) and is re-read coherently.
-template <int PER>
-__device__ void read_done_to_lds(const uint64_t* src, int n, uint32_t tag, float* dst) {
-  uint64_t v[PER];
+// Read tagged values after their producers have all signalled completion: na
+// words of a into da and nb words of b into db, every load issued before any is
+// checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32 workgroups
+// of an XCD share one fetch from memory; a word still carrying an old tag comes
+// from a stale cached line (the buffer slot was last used several calls ago) and
+// is re-read coherently.
+template <int PA, int PB>
+__device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uint64_t* b, int nb,
+                                 float* db, uint32_t tag) {
+  uint64_t v[PA + PB];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = threadIdx.x + j * kLB;
-    v[j] = i < n ? src[i] : 0;
+  for (int j = 0; j < PA + PB; ++j) {
+    const bool in_a = j < PA;
+    const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
+    v[j] = i < (in_a ? na : nb) ? (in_a ? a : b)[i] : 0;
   }
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = threadIdx.x + j * kLB;
-    if (i < n) {
+  for (int j = 0; j < PA + PB; ++j) {
+    const bool in_a = j < PA;
+    const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
+    if (i < (in_a ? na : nb)) {
       uint64_t w = v[j];
-      if ((uint32_t)(w >> 32) != tag) w = tag_get(const_cast<uint64_t*>(src) + i);
-      dst[i] = __uint_as_float((uint32_t)w);
+      if ((uint32_t)(w >> 32) != tag) w = tag_get(const_cast<uint64_t*>(in_a ? a : b) + i);
+      (in_a ? da : db)[i] = __uint_as_float((uint32_t)w);
     }
   }
 }
@@ -551,8 +556,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // Every workgroup has read the epoch before tagging its flag: advance it.
   if (wg == 0 && threadIdx.x == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB>(hr, K * I, tag, s_h);
-  read_done_to_lds<(I + kLB - 1) / kLB>(hs, I, tag, s_h + kFusedMaxK * I);
+  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
+      hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag);
   __syncthreads();
   // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
   // two vectors; unused routed slots hold stale values whose planes are not read)
