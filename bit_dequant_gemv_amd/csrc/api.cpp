@@ -252,7 +252,8 @@ int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* 
   if (rc) return rc;
   if (T < 1 || T > qmoe::kMaxBatch) return fail(QMOE_ESHAPE, "T must be in [1, %d]", qmoe::kMaxBatch);
   if ((rc = check_vec(x, "x"))) return rc;
-  if (!residual || !out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  if ((rc = check_vec(residual, "residual")) || (rc = check_vec(out, "out"))) return rc;
+  if (!topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
   if (out == x) return fail(QMOE_EINVAL, "out must not alias x");
   const size_t need = qmoe_workspace_bytes(L, T);
   if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);

@@ -134,7 +134,9 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     }
   }
   // the last thread holds the totals: the shared expert's chunks follow
+  __shared__ int routed;  // routed pairs in all
   if (threadIdx.x == blockDim.x - 1) {
+    routed = ep;
     int g = eg;
     for (int c = 0; c < T; c += kChunk) {
       G.group_expert[g] = -1;
@@ -154,13 +156,6 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     G.pair_list[off[e] + r] = p;
   }
   // the shared expert's pairs follow every routed pair
-  __shared__ int routed;
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) acc += cnt[e];
-    routed = acc;
-  }
-  __syncthreads();
   for (int t = threadIdx.x; t < T; t += blockDim.x) G.pair_list[routed + t] = P + t;
 }
 
@@ -292,8 +287,9 @@ __global__ __launch_bounds__(kBB) void k_bdown(PoolArgsB P, GroupTables G,
   }
 }
 
-// grid (T, column slices): gamma_t = sigmoid(g . x_t) (each slice computes it
-// again), then the combine of the slice's columns
+// grid (T, column slices of kCombineCols): gamma_t = sigmoid(g . x_t) (each slice
+// computes it again), then the combine of the slice's columns, four per thread
+// (H % 4 == 0)
 constexpr int kCombineCols = 1024;
 __global__ __launch_bounds__(kBB) void k_bcombine(const float* __restrict__ y,
                                                   const float* __restrict__ w,
@@ -305,21 +301,39 @@ __global__ __launch_bounds__(kBB) void k_bcombine(const float* __restrict__ y,
   const int t = blockIdx.x;
   const float* xt = x + (int64_t)t * H;
   float d = 0.f;
-  for (int i = threadIdx.x; i < H; i += kBB) d += __uint_as_float((uint32_t)g[i] << 16) * xt[i];
+  for (int i = 4 * threadIdx.x; i < H; i += 4 * kBB) {
+    const float4 xv = *reinterpret_cast<const float4*>(xt + i);
+    const uint2 gv = *reinterpret_cast<const uint2*>(g + i);
+    d = fmaf(bf16_lo(gv.x), xv.x, d);
+    d = fmaf(bf16_hi(gv.x), xv.y, d);
+    d = fmaf(bf16_lo(gv.y), xv.z, d);
+    d = fmaf(bf16_hi(gv.y), xv.w, d);
+  }
   d = group_sum<64>(d);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
   __syncthreads();
   float tot = 0.f;
   for (int i = 0; i < kBB / 64; ++i) tot += red[i];
   const float gamma = sigmoid_f(tot);
-  const float* ys = y + ((int64_t)T * K + t) * H;
-  const int n1 = min(H, (int)(blockIdx.y + 1) * kCombineCols);
-  for (int n = blockIdx.y * kCombineCols + threadIdx.x; n < n1; n += kBB) {
-    float acc = residual[(int64_t)t * H + n];
-    for (int k = 0; k < K; ++k) acc = fmaf(w[t * K + k], y[((int64_t)t * K + k) * H + n], acc);
-    out[(int64_t)t * H + n] = fmaf(gamma, ys[n], acc);
+  const int n = blockIdx.y * kCombineCols + 4 * threadIdx.x;
+  if (n >= H) return;
+  float4 acc = *reinterpret_cast<const float4*>(residual + (int64_t)t * H + n);
+  for (int k = 0; k < K; ++k) {
+    const float wk = w[t * K + k];
+    const float4 v = *reinterpret_cast<const float4*>(y + ((int64_t)t * K + k) * H + n);
+    acc.x = fmaf(wk, v.x, acc.x);
+    acc.y = fmaf(wk, v.y, acc.y);
+    acc.z = fmaf(wk, v.z, acc.z);
+    acc.w = fmaf(wk, v.w, acc.w);
   }
+  const float4 v = *reinterpret_cast<const float4*>(y + ((int64_t)T * K + t) * H + n);
+  acc.x = fmaf(gamma, v.x, acc.x);
+  acc.y = fmaf(gamma, v.y, acc.y);
+  acc.z = fmaf(gamma, v.z, acc.z);
+  acc.w = fmaf(gamma, v.w, acc.w);
+  *reinterpret_cast<float4*>(out + (int64_t)t * H + n) = acc;
 }
+static_assert(kCombineCols == 4 * kBB, "one float4 of columns per thread");
 
 template <int BITS, int LG, int CPL>
 void run_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp, float* h,

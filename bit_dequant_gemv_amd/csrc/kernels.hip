@@ -442,6 +442,123 @@ __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logit
   }
 }
 
+// Router GEMV for a batch of tokens: the router rows are read once per 16 tokens
+// instead of once per token.  grid (ceil(E/8), ceil(T/16)), 256 threads: the block
+// owns 8 experts x 16 tokens; half-wave hw owns a 4-expert x 4-token tile and its
+// 32 lanes split H, lane l taking k = 128 i + 4 l .. +3, so that one load
+// instruction covers 512 contiguous bytes; the 32 partial sums of each output are
+// added across the half-wave at the end.  Needs H % 128 == 0.
+constexpr int kRtE = 8, kRtT = 16;
+__global__ __launch_bounds__(kBlock) void k_router_tiled(const uint16_t* __restrict__ router,
+                                                         const float* __restrict__ x,
+                                                         float* __restrict__ logits, int T, int E,
+                                                         int H) {
+  const int lane = threadIdx.x & 63, hw = threadIdx.x >> 5, l = lane & 31;
+  const int e0 = blockIdx.x * kRtE + (hw & 1) * 4, t0 = blockIdx.y * kRtT + (hw >> 1) * 4;
+  const uint16_t* rp[4];
+  const float* xp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // rows past the end repeat the last one; never stored
+    rp[j] = router + (int64_t)min(e0 + j, E - 1) * H + 4 * l;
+    xp[j] = x + (int64_t)min(t0 + j, T - 1) * H + 4 * l;
+  }
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+#pragma unroll 2
+  for (int k = 0; k < H; k += 128) {
+    float4 xv[4];
+    uint2 rv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[j] = *reinterpret_cast<const float4*>(xp[j] + k);
+      rv[j] = *reinterpret_cast<const uint2*>(rp[j] + k);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float r0 = bf16_lo(rv[a].x), r1 = bf16_hi(rv[a].x);
+      const float r2 = bf16_lo(rv[a].y), r3 = bf16_hi(rv[a].y);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[a][b] = fmaf(r0, xv[b].x, acc[a][b]);
+        acc[a][b] = fmaf(r1, xv[b].y, acc[a][b]);
+        acc[a][b] = fmaf(r2, xv[b].z, acc[a][b]);
+        acc[a][b] = fmaf(r3, xv[b].w, acc[a][b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float v = group_sum_last<32>(acc[a][b]);
+      if (l == 31 && e0 + a < E && t0 + b < T) logits[(int64_t)(t0 + b) * E + e0 + a] = v;
+    }
+}
+
+// Top-K with renormalised softmax, one wave per token (4 tokens per workgroup):
+// K rounds of a wave-wide arg-max over order-preserving keys (larger logit, then
+// lower index; -0 counts as +0).  Lane l holds experts l + 64 j, j < PER.
+template <int PER>
+__global__ __launch_bounds__(kBlock) void k_topk_wave(const float* __restrict__ logits, int T,
+                                                      int E, int K, int32_t* __restrict__ idx,
+                                                      float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* lt = logits + (int64_t)t * E;
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? order_key(__float_as_uint(lt[e])) : 0u;
+  }
+  uint32_t bk = 0, bi = 0xFFFFFFFFu;
+  auto best = [&]() {
+    bk = 0;
+    bi = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (key[j] > bk) {  // strictly larger: the lower index wins a tie
+        bk = key[j];
+        bi = lane + 64 * j;
+      }
+  };
+  best();
+  uint32_t pk[kMaxTopK], pi[kMaxTopK];
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    pk[r] = 0;
+    pi[r] = 0xFFFFFFFFu;
+    if (r < K) {
+      wave_argmax(bk, bi, pk[r], pi[r]);
+      if (pk[r] != 0 && bi == pi[r]) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          if (lane + 64 * j == (int)pi[r]) key[j] = 0;
+        best();
+      }
+    }
+  }
+  // softmax over the picks (uniform values); lane r writes pick r
+  const float m = key_value(pk[0]);
+  float ex[kMaxTopK], sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    ex[r] = r < K ? expf(key_value(pk[r]) - m) : 0.f;
+    sum += ex[r];
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r)
+    if (r < K && lane == r) {
+      idx[(int64_t)t * K + r] = (int32_t)pi[r];
+      w[(int64_t)t * K + r] = ex[r] * inv;
+    }
+}
+
 template <int LG, int CPL>
 hipError_t run_router(const uint16_t* router, const float* x, float* logits, int T, int E, int H,
                       hipStream_t s) {
@@ -523,7 +640,11 @@ hipError_t launch_router_topk(const uint16_t* router, const float* x, int T, int
   if (T == 0) return hipSuccess;
   const int C = H / 8;
   hipError_t err;
-  if (C <= 8) err = run_router<8, 1>(router, x, logits, T, E, H, s);
+  if (T >= 8 && H % 128 == 0) {
+    hipLaunchKernelGGL(k_router_tiled, dim3(ceil_div(E, kRtE), ceil_div(T, kRtT)), dim3(kBlock), 0,
+                       s, router, x, logits, T, E, H);
+    err = hipGetLastError();
+  } else if (C <= 8) err = run_router<8, 1>(router, x, logits, T, E, H, s);
   else if (C <= 16) err = run_router<16, 1>(router, x, logits, T, E, H, s);
   else if (C <= 32) err = run_router<32, 1>(router, x, logits, T, E, H, s);
   else if (C <= 64) err = run_router<64, 1>(router, x, logits, T, E, H, s);
@@ -532,7 +653,10 @@ hipError_t launch_router_topk(const uint16_t* router, const float* x, int T, int
   else if (C <= 512) err = run_router<64, 8>(router, x, logits, T, E, H, s);
   else err = run_router<64, 16>(router, x, logits, T, E, H, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(kBlock), 0, s, logits, E, K, idx, w);
+  const dim3 tg(ceil_div(T, kBlock / 64));
+  if (E <= 512) hipLaunchKernelGGL(k_topk_wave<8>, tg, dim3(kBlock), 0, s, logits, T, E, K, idx, w);
+  else if (E <= 1024) hipLaunchKernelGGL(k_topk_wave<16>, tg, dim3(kBlock), 0, s, logits, T, E, K, idx, w);
+  else hipLaunchKernelGGL(k_topk, dim3(T), dim3(kBlock), 0, s, logits, E, K, idx, w);
   return hipGetLastError();
 }
 

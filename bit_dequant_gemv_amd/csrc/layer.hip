@@ -126,17 +126,6 @@ __device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uin
   }
 }
 
-// Order-preserving u32 key of a float's bits (larger key = larger value; -0 is
-// mapped to +0 first, so the two zeros tie).  Key 0 means "no expert": no finite
-// value maps to it.
-__device__ __forceinline__ uint32_t order_key(uint32_t b) {
-  b = b == 0x80000000u ? 0u : b;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
 __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float a0 = 0.f, a1 = 0.f;

@@ -111,6 +111,31 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(a, b);
 }
 
+// Order-preserving u32 key of a float's bits (larger key = larger value; -0 is
+// mapped to +0 first, so the two zeros tie).  Key 0 means "no expert": no finite
+// value maps to it.
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  b = b == 0x80000000u ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Wave-wide arg-max of (key, index) pairs: m = the largest key (0 when every lane
+// holds 0, i.e. nothing), wi = the smallest index among the lanes holding m
+// (0xFFFFFFFF if none).  Both results are wave-uniform.
+__device__ __forceinline__ void wave_argmax(uint32_t k, uint32_t i, uint32_t& m, uint32_t& wi) {
+  m = wave_max_u32(k);
+  const uint64_t b = __builtin_amdgcn_ballot_w64(k == m && m != 0u);
+  if (b == 0)
+    wi = 0xFFFFFFFFu;
+  else if ((b & (b - 1)) == 0)  // one lane: the common case
+    wi = (uint32_t)__builtin_amdgcn_readlane((int)i, __builtin_ctzll(b));
+  else  // equal keys: the lower index
+    wi = wave_min_u32(k == m ? i : 0xFFFFFFFFu);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

@@ -180,7 +180,8 @@ int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* nor
  * Batched decode of T tokens through one layer (row t equals moe_layer_forward on
  * token t): tokens are grouped per routed expert (histogram, scan, stable scatter)
  * so each active expert's weights are read once per batch.
- *   x, residual, out: device float [T][H] (out must not alias x; it may alias residual);
+ *   x, residual, out: device float [T][H], 16-byte aligned (out must not alias x; it
+ *   may alias residual);
  *   topk_idx/topk_w: device [T][K] (written).
  *   ws: at least qmoe_workspace_bytes(L, T) bytes, 256-byte aligned, zero-filled
  *   before its first use (the same workspace may serve moe_layer_forward).

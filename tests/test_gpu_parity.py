@@ -147,7 +147,10 @@ def test_expert_ffn_bad_index_gives_nan(q):
 # router + top-K, combine, RMSNorm
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("E,H,K,T", [(512, 4096, 4, 5), (64, 1024, 8, 3), (10, 256, 3, 2), (4096, 512, 2, 1)])
+# T >= 8 takes the token-tiled router (ragged expert and token tiles included) and,
+# for E <= 1024, the wave-per-token top-K
+@pytest.mark.parametrize("E,H,K,T", [(512, 4096, 4, 5), (64, 1024, 8, 3), (10, 256, 3, 2), (4096, 512, 2, 1),
+                                     (512, 4096, 4, 64), (1000, 1024, 8, 9), (2048, 512, 2, 20)])
 def test_router_topk_parity(q, E, H, K, T):
     say("router_topk", E, H, K, T)
     seed = 2000 + E
@@ -168,8 +171,9 @@ def test_router_topk_parity(q, E, H, K, T):
         say("  token", t, "near-tie exemptions", ex)
 
 
-def test_router_exact_ties_go_to_lower_index(q):
-    say("router ties")
+@pytest.mark.parametrize("T", [1, 8])
+def test_router_exact_ties_go_to_lower_index(q, T):
+    say("router ties", T)
     E, H = 512, 4096
     R = synth.router(31, 0, E, H).copy()
     X = host_x(31, 0, H)
@@ -178,10 +182,11 @@ def test_router_exact_ties_go_to_lower_index(q):
     R[300] = R[7]
     R[450] = R[7]
     idx, w, _ = q.moe_router_topk(torch.from_numpy(R.view(np.int16)).cuda(),
-                                  torch.from_numpy(X).cuda(), 4)
-    got = idx.cpu().numpy()[0].tolist()
-    assert got[:3] == [7, 300, 450], got
-    np.testing.assert_allclose(w.cpu().numpy()[0][:3], w.cpu().numpy()[0][0], rtol=0)
+                                  torch.from_numpy(np.tile(X, (T, 1))).cuda(), 4)
+    for t in range(T):
+        got = idx.cpu().numpy()[t].tolist()
+        assert got[:3] == [7, 300, 450], got
+        np.testing.assert_allclose(w.cpu().numpy()[t][:3], w.cpu().numpy()[t][0], rtol=0)
 
 
 def test_combine_parity(q):
