@@ -79,11 +79,11 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
                                                 int E, GroupTables G) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts];
-  __shared__ int sidx[kMaxBatch * kMaxTopK];
+  __shared__ __align__(16) int sidx[kMaxBatch * kMaxTopK + 16];  // + padding of -1
   __shared__ int wsum[16];
   const int P = T * K;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-  for (int p = threadIdx.x; p < P; p += blockDim.x) sidx[p] = idx[p];
+  for (int p = threadIdx.x; p < P + 16; p += blockDim.x) sidx[p] = p < P ? idx[p] : -1;
   __syncthreads();
   for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int e = sidx[p];
@@ -147,12 +147,24 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     G.n_groups[0] = g;
   }
   __syncthreads();
-  // stable scatter: rank of pair p among earlier pairs of the same expert
+  // stable scatter: rank of pair p among earlier pairs of the same expert (the
+  // list is read 16 entries at a time; entries at or past p do not count)
+  const int4* s4 = reinterpret_cast<const int4*>(sidx);
   for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int e = sidx[p];
     if ((unsigned)e >= (unsigned)E) continue;
     int r = 0;
-    for (int q = 0; q < p; ++q) r += sidx[q] == e;
+    for (int q0 = 0; q0 < p; q0 += 16) {
+      int4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = s4[q0 / 4 + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 4 * u;
+        r += (q < p && v[u].x == e) + (q + 1 < p && v[u].y == e) + (q + 2 < p && v[u].z == e) +
+             (q + 3 < p && v[u].w == e);
+      }
+    }
     G.pair_list[off[e] + r] = p;
   }
   // the shared expert's pairs follow every routed pair
@@ -410,11 +422,15 @@ hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float
   uint32_t* hp = reinterpret_cast<uint32_t*>(wsb + b.hp);
   float* y = reinterpret_cast<float*>(wsb + b.y);
   const GroupTables G = group_tables(wsb, b, T, K);
-  hipError_t err = launch_router_topk(L.router, x, T, H, E, K, logits, idx, w, s);
+  bool prepped = false;  // the router can build the x planes on the way
+  hipError_t err = launch_router_topk(L.router, x, T, H, E, K, logits, idx, w, s, bits, xp,
+                                      bits == 4 ? plane_words<4>(H) : plane_words<2>(H), &prepped);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, idx, T, K, E, G);
-  if (bits == 4) run_prep<4>(x, T, H, xp, s);
-  else run_prep<2>(x, T, H, xp, s);
+  if (!prepped) {
+    if (bits == 4) run_prep<4>(x, T, H, xp, s);
+    else run_prep<2>(x, T, H, xp, s);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const qmoe_expert_offsets o = expert_offsets(H, I, bits);
   PoolArgsB P;

@@ -443,24 +443,35 @@ __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logit
 }
 
 // Router GEMV for a batch of tokens: the router rows are read once per 16 tokens
-// instead of once per token.  grid (ceil(E/8), ceil(T/16)), 256 threads: the block
-// owns 8 experts x 16 tokens; half-wave hw owns a 4-expert x 4-token tile and its
-// 32 lanes split H, lane l taking k = 128 i + 4 l .. +3, so that one load
-// instruction covers 512 contiguous bytes; the 32 partial sums of each output are
-// added across the half-wave at the end.  Needs H % 128 == 0.
+// instead of once per token.  grid (ceil(E/8), ceil(T/16)), 256*G threads: the
+// block owns 8 experts x 16 tokens and its G groups of 4 waves split H into G
+// slices.  In a group, half-wave hw owns a 4-expert x 4-token tile and its 32
+// lanes split the slice, lane l taking k = 128 i + 4 l .. +3, so that one load
+// instruction covers 512 contiguous bytes.  The 32 lane sums of an output are
+// added across the half-wave, then the G slice sums in group order (in LDS).
+// Needs (H / G) % 128 == 0.  With BITS > 0 the workgroups of the first 16 columns
+// also write the fixed-point planes of one token of their tile each (planes of
+// token t at xplanes + t*pw: C*PW plane words, C scales, C sums), which the
+// batched layer takes next.
 constexpr int kRtE = 8, kRtT = 16;
-__global__ __launch_bounds__(kBlock) void k_router_tiled(const uint16_t* __restrict__ router,
-                                                         const float* __restrict__ x,
-                                                         float* __restrict__ logits, int T, int E,
-                                                         int H) {
-  const int lane = threadIdx.x & 63, hw = threadIdx.x >> 5, l = lane & 31;
-  const int e0 = blockIdx.x * kRtE + (hw & 1) * 4, t0 = blockIdx.y * kRtT + (hw >> 1) * 4;
+template <int G, int BITS>
+__global__ __launch_bounds__(kBlock * G) void k_router_tiled(const uint16_t* __restrict__ router,
+                                                             const float* __restrict__ x,
+                                                             float* __restrict__ logits, int T,
+                                                             int E, int H, uint32_t* xplanes,
+                                                             int pw) {
+  __shared__ float red[G][kRtE * kRtT];
+  const int grp = threadIdx.x / kBlock, tid = threadIdx.x % kBlock;
+  const int lane = tid & 63, hw = tid >> 5, l = lane & 31;
+  const int le = (hw & 1) * 4, lt = (hw >> 1) * 4;  // the tile's first local expert / token
+  const int e0 = blockIdx.x * kRtE + le, t0 = blockIdx.y * kRtT + lt;
+  const int hs = H / G;
   const uint16_t* rp[4];
   const float* xp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // rows past the end repeat the last one; never stored
-    rp[j] = router + (int64_t)min(e0 + j, E - 1) * H + 4 * l;
-    xp[j] = x + (int64_t)min(t0 + j, T - 1) * H + 4 * l;
+    rp[j] = router + (int64_t)min(e0 + j, E - 1) * H + grp * hs + 4 * l;
+    xp[j] = x + (int64_t)min(t0 + j, T - 1) * H + grp * hs + 4 * l;
   }
   float acc[4][4];
 #pragma unroll
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void k_router_tiled(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
 #pragma unroll 2
-  for (int k = 0; k < H; k += 128) {
+  for (int k = 0; k < hs; k += 128) {
     float4 xv[4];
     uint2 rv[4];
 #pragma unroll
@@ -494,8 +505,26 @@ __global__ __launch_bounds__(kBlock) void k_router_tiled(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float v = group_sum_last<32>(acc[a][b]);
-      if (l == 31 && e0 + a < E && t0 + b < T) logits[(int64_t)(t0 + b) * E + e0 + a] = v;
+      if (l == 31) red[grp][(le + a) * kRtT + lt + b] = v;
     }
+  __syncthreads();
+  if ((int)threadIdx.x < kRtE * kRtT) {
+    const int e = blockIdx.x * kRtE + (int)threadIdx.x / kRtT;
+    const int t = blockIdx.y * kRtT + (int)threadIdx.x % kRtT;
+    float v = red[0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < G; ++g) v += red[g][threadIdx.x];
+    if (e < E && t < T) logits[(int64_t)t * E + e] = v;
+  }
+  if constexpr (BITS > 0) {
+    const int t = blockIdx.y * kRtT + (int)blockIdx.x;
+    if ((int)blockIdx.x < kRtT && t < T) {  // uniform per workgroup
+      uint32_t* planes = xplanes + (int64_t)t * pw;
+      const int C = H / QTraits<BITS>::EPC;
+      float* scl = reinterpret_cast<float*>(planes + C * QTraits<BITS>::PW);
+      prep_x_coop<BITS>(x + (int64_t)t * H, H, planes, scl, scl + C, threadIdx.x, blockDim.x);
+    }
+  }
 }
 
 // Top-K with renormalised softmax, one wave per token (4 tokens per workgroup):
@@ -636,14 +665,30 @@ hipError_t launch_ffn(const qmoe_expert_pool& pool, const int32_t* idx, int n, c
 }
 
 hipError_t launch_router_topk(const uint16_t* router, const float* x, int T, int H, int E, int K,
-                              float* logits, int32_t* idx, float* w, hipStream_t s) {
+                              float* logits, int32_t* idx, float* w, hipStream_t s, int prep_bits,
+                              uint32_t* xplanes, int pw, bool* prepped) {
+  if (prepped) *prepped = false;
   if (T == 0) return hipSuccess;
   const int C = H / 8;
   hipError_t err;
   if (T >= 8 && H % 128 == 0) {
-    hipLaunchKernelGGL(k_router_tiled, dim3(ceil_div(E, kRtE), ceil_div(T, kRtT)), dim3(kBlock), 0,
-                       s, router, x, logits, T, E, H);
+    // the planes need a workgroup per token in the first 16 columns: E >= 8*15+1
+    const bool prep = prep_bits && xplanes && H % 512 == 0 && E > kRtE * (kRtT - 1);
+    dim3 grid(ceil_div(E, kRtE), ceil_div(T, kRtT));
+    if (prep && prep_bits == 4)
+      hipLaunchKernelGGL((k_router_tiled<4, 4>), grid, dim3(4 * kBlock), 0, s, router, x, logits, T, E,
+                         H, xplanes, pw);
+    else if (prep)
+      hipLaunchKernelGGL((k_router_tiled<4, 2>), grid, dim3(4 * kBlock), 0, s, router, x, logits, T, E,
+                         H, xplanes, pw);
+    else if (H % 512 == 0)
+      hipLaunchKernelGGL((k_router_tiled<4, 0>), grid, dim3(4 * kBlock), 0, s, router, x, logits, T, E,
+                         H, nullptr, 0);
+    else
+      hipLaunchKernelGGL((k_router_tiled<1, 0>), grid, dim3(kBlock), 0, s, router, x, logits, T, E, H,
+                         nullptr, 0);
     err = hipGetLastError();
+    if (prepped) *prepped = prep && err == hipSuccess;
   } else if (C <= 8) err = run_router<8, 1>(router, x, logits, T, E, H, s);
   else if (C <= 16) err = run_router<16, 1>(router, x, logits, T, E, H, s);
   else if (C <= 32) err = run_router<32, 1>(router, x, logits, T, E, H, s);

@@ -23,8 +23,12 @@ hipError_t launch_qgemv(int bits, const uint8_t* codes, const uint32_t* sb, cons
 hipError_t launch_ffn(const qmoe_expert_pool& pool, const int32_t* idx, int n, const float* x,
                       int64_t x_stride, float* y, float* h_ws, hipStream_t s);
 
+// prep_bits = 4 or 2 with xplanes: the router may also write the fixed-point x
+// planes of every token (pw words per token); *prepped says whether it did.
 hipError_t launch_router_topk(const uint16_t* router, const float* x, int T, int H, int E, int K,
-                              float* logits, int32_t* idx, float* w, hipStream_t s);
+                              float* logits, int32_t* idx, float* w, hipStream_t s,
+                              int prep_bits = 0, uint32_t* xplanes = nullptr, int pw = 0,
+                              bool* prepped = nullptr);
 
 hipError_t launch_combine(const float* y_routed, const float* w, const float* y_shared,
                           const uint16_t* g, const float* x, const float* residual, float* out,
