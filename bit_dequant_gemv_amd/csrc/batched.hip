@@ -351,7 +351,7 @@ template <int BITS, int LG, int CPL>
 void run_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp, float* h,
                  hipStream_t s) {
   constexpr int RPW = 64 / LG;
-  constexpr int NR = CPL >= 4 ? 2 : 4;
+  constexpr int NR = CPL >= 2 ? 2 : 4;
   const int rpb = (kBB / 64) * NR * RPW;
   hipLaunchKernelGGL((k_bgateup<BITS, LG, CPL, NR>), dim3(ceil_div(P.I, rpb), gm), dim3(kBB), 0, s,
                      P, G, xp, h, rpb);
