@@ -135,6 +135,19 @@ def capture_graphs(torch, fn_list, per_graph):
     return graphs
 
 
+def warm_for(torch, fn, seconds):
+    """Run fn repeatedly for at least `seconds` of wall time (then synchronise), so
+    that a bandwidth measurement starts in steady state."""
+    import time
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_graphs(torch, graphs, n_replays, warmup_replays, tail=None):
     """Replay graphs round-robin (plus one optional tail graph) between two
     synchronisations; returns the seconds between the events around the timed
@@ -238,7 +251,8 @@ def run_qgemv_stream(torch, q, synth):
     y = torch.empty(n, rows, dtype=torch.float32, device="cuda")
     calls = [(lambda i=i: q.qgemv_w4(codes[i % n], sb[i % n], x, y[i % n])) for i in range(16)]
     graphs = capture_graphs(torch, calls, 16)
-    reps = 8
+    warm_for(torch, lambda: graphs[0].replay(), 0.1)  # clocks and page translations settle
+    reps = 32
     dt = time_graphs(torch, graphs, reps, 2)
     per = rows * cols // 2 + rows * (cols // 64) * 4 + cols * 4 + rows * 4
     launches = 16 * reps
@@ -253,9 +267,7 @@ def run_copy(torch):
     n = 1 << 28
     a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
-    for _ in range(2):
-        b.copy_(a)
-    torch.cuda.synchronize()
+    warm_for(torch, lambda: b.copy_(a), 0.1)
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)

@@ -62,18 +62,19 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ co
   RowDot<BITS, LG, CPL> rd;
   load_x_shared<BITS, LG, CPL>(rd, x, cols, C, gl);
   const int64_t step = (int64_t)gridDim.x * (kBlock / 64) * RPW * R;
+  // Unconditional loads (a row past the end reads the last row, which every such
+  // wave shares in cache), so that the dots of one pass wait only for that pass's
+  // rows and the next pass's loads stay in flight meanwhile.
   auto fetch_rows = [&](int64_t base, uint4 (&q)[R][CPL], uint32_t (&s)[R][CPL]) {
     const uint8_t* crow[R];
     const uint32_t* srow[R];
-    bool ok[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t row = base + r * RPW + sub;
-      ok[r] = row < rows;
-      crow[r] = codes + (ok[r] ? row : 0) * rowbytes;
-      srow[r] = sb + (ok[r] ? row : 0) * G;
+      const int64_t row = min(base + r * RPW + sub, (int64_t)rows - 1);
+      crow[r] = codes + row * rowbytes;
+      srow[r] = sb + row * G;
     }
-    rd.template fetch<R>(crow, srow, ok, C, gl, q, s);
+    rd.template fetch_clamped<R>(crow, srow, C, gl, q, s);
   };
   int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
   uint4 q[R][CPL];
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ co
   for (; base < rows; base += step) {
     uint4 qn[R][CPL];
     uint32_t sn[R][CPL];
-    if (base + step < rows) fetch_rows(base + step, qn, sn);
+    fetch_rows(base + step, qn, sn);
     float p[R];
     rd.template dots<R>(q, s, p);
 #pragma unroll

@@ -584,6 +584,24 @@ struct RowDot {
     }
   }
 
+  // Loads with no conditions at all: a chunk past the row (gl + i*LG >= C) reads the
+  // row's last chunk instead, which adds nothing since the x planes of such a chunk
+  // are zero (load_x / load_prepped); every row pointer must be valid.
+  template <int R>
+  __device__ __forceinline__ void fetch_clamped(const uint8_t* const* crow,
+                                                const uint32_t* const* srow, int C, int gl,
+                                                uint4 (&q)[R][CPL], uint32_t (&s)[R][CPL]) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t c = (uint32_t)min(gl + i * LG, C - 1);
+        q[r][i] = ld_stream16(crow[r] + 16u * c);
+        s[r][i] = ld_stream4(srow[r] + c / QTraits<BITS>::CPG);
+      }
+    }
+  }
+
   // Lane partial sums of R fetched rows (before the group reduction).
   template <int R>
   __device__ __forceinline__ void dots(const uint4 (&q)[R][CPL], const uint32_t (&s)[R][CPL],
