@@ -155,6 +155,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   constexpr int64_t RBI = (int64_t)I * BITS / 8;
   constexpr int DITEMS = (kRB + RPWI - 1) / RPWI;  // down items per expert per workgroup
   static_assert(DITEMS <= kLW, "one shared down item per wave");
+  static_assert(kRB % RPWI == 0, "a down pass never runs past the workgroup's rows");
   constexpr int MAXR = (kFusedMaxK * DITEMS + kLW - 1) / kLW;  // routed down items per wave
   constexpr int NSP = I / RPWH;                 // shared gate/up items
   constexpr int CRQ = H / 32;                   // 16-byte router chunks per quarter row
@@ -237,11 +238,13 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // shared-expert down rows of this workgroup: slot 0 of waves 0..DITEMS-1
   const int nl_s = wv * RPWI + subi;
   const bool sd_ok = wv < DITEMS && nl_s < kRB && row0 + nl_s < H;
-  if (sd_ok) {
+  if (sd_ok) {  // a wave-uniform row base plus a 32-bit lane offset
     const int sl = wv * kSlots;
-    dma16(A.sblk + A.off_d + (row0 + nl_s) * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
-    dma4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (row0 + nl_s) * GI +
-             gli / QTraits<BITS>::CPG,
+    const int rb = row0 + wv * RPWI;
+    dma16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli),
+          lds_ptr(&s_dq[sl * 64]));
+    dma4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
+             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG),
          lds_ptr(&s_ds[sl * 64]));
   }
   const float resid = (int)threadIdx.x < kRB ? A.residual[row0 + threadIdx.x] : 0.f;
@@ -511,13 +514,16 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     const int t = wv * MAXR + m;
     const int k = t / DITEMS, d = t % DITEMS;
     const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
-    const int nl = d * RPWI + subi;
-    const bool ok = (unsigned)e < (unsigned)E && nl < kRB && row0 + nl < H;
+    // wave-uniform choices: every output row of the pass lies inside H (H is a
+    // multiple of kRB), so a valid expert reads rows row0 + d*RPWI + subi
+    const bool ok = (unsigned)e < (unsigned)E;
     const uint8_t* blk = ok ? A.rbase + (int64_t)e * A.rstride : A.sblk;
-    const int rowd = ok ? row0 + nl : 0;
+    const int rb = ok ? row0 + d * RPWI : 0;
     const int sl = wv * kSlots + 1 + m;
-    dma16(blk + A.off_d + rowd * RBI + 16 * gli, lds_ptr(&s_dq[sl * 64]));
-    dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + rowd * GI + gli / QTraits<BITS>::CPG,
+    dma16(blk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli),
+          lds_ptr(&s_dq[sl * 64]));
+    dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)rb * GI +
+             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG),
          lds_ptr(&s_ds[sl * 64]));
   }
   // completion: every store of this workgroup acknowledged (all vector memory

@@ -64,8 +64,9 @@ struct QTraits<2> {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// (the hardware reciprocal, within 1 ulp, instead of a full division)
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ uint32_t udot8(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_udot8(a, b, c, false);
@@ -258,8 +259,12 @@ __device__ __forceinline__ void prep_word(const float* v, float f, uint32_t* out
 
 // Integer total of one chunk: sum_k q_k X_k (times 4 for 2-bit codes) as a float.
 __device__ __forceinline__ float combine_planes(const uint32_t (&a)[6], uint32_t qs) {
-  const uint32_t low = a[0] + (a[1] << 4) + (a[2] << 8) + (a[3] << 12) + (a[4] << 16);
-  const int top = (int)a[5] - 8 * (int)qs;
+  // Horner form: four shift-adds (each plane sum is < 2^13, so low < 2^30)
+  uint32_t low = (a[4] << 4) + a[3];
+  low = (low << 4) + a[2];
+  low = (low << 4) + a[1];
+  low = (low << 4) + a[0];
+  const int top = (int)a[5] + (int)qs * -8;
   return fmaf((float)top, 1048576.0f, (float)(int)low);
 }
 
