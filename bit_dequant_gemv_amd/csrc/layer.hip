@@ -535,7 +535,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   if (threadIdx.x == 0) tag_put(A.flags + wg, 0.f, tag);
 
   // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
-  //         routed down rows (float dots from h in LDS, codes from the LDS DMA);
+  //         routed down rows (integer dots against the planes of h, codes from the
+  //         LDS DMA);
   //         combine
   if ((int)threadIdx.x < NB) {
     uint32_t spins = 0;
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
   // two vectors; unused routed slots hold stale values whose planes are not read)
   prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, threadIdx.x, kLB);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 6) has landed
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 7) has landed
   __syncthreads();
   const float gpart = group_sum_last<64>(bf16_chunk_dot(gq, gx));
   if (lane == 63) s_rv[wv] = gpart;
