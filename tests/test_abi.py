@@ -84,6 +84,12 @@ def test_invalid_arguments_are_rejected_before_launch():
         q.QMOE_ESHAPE
     assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 256, 512, 0, 16, 16, 256, need, None) == \
         q.QMOE_ESHAPE
+    # batched: residual and out are read and written as float4s
+    need2 = lib.qmoe_workspace_bytes(ctypes.byref(L), 2)
+    assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 260, 512, 2, 16, 16, 256, need2, None) == \
+        q.QMOE_EALIGN
+    assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 512, 516, 2, 16, 16, 256, need2, None) == \
+        q.QMOE_EALIGN
     assert lib.rmsnorm_f32(16, 16, -1.0, 4, 16, None) == q.QMOE_EINVAL
     assert lib.qmoe_workspace_bytes(ctypes.byref(L), 0) == 0
     assert lib.qmoe_strerror(q.QMOE_EWORKSPACE) == b"workspace too small"
