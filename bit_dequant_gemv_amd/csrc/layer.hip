@@ -53,6 +53,7 @@ constexpr int kLW = kLB / 64;    // waves per workgroup
 constexpr int kRB = 16;          // output rows per workgroup
 constexpr int kFusedMaxK = 4;
 constexpr int kFusedMaxE = 2048;
+static_assert(kFusedMaxE % 64 == 0, "the ranking wave reads the candidate list 64 at a time");
 constexpr uint32_t kSpinLimit = 1u << 18;
 constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see step 8
 
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __shared__ float s_rv[kLW];
   __shared__ uint32_t s_wmax[kLW];             // top-K: largest key of each wave
   __shared__ uint32_t s_ncand;                 // number of candidates
-  __shared__ uint64_t s_cand[kFusedMaxE + 8];  // candidates: key << 32 | expert (+ padding)
+  __shared__ uint64_t s_cand[kFusedMaxE];      // candidates: key << 32 | ~expert
   __shared__ uint64_t s_pick[kFusedMaxK];      // the picks, in rank order
   __shared__ uint4 s_dq[kLW * kSlots * 64];     // down-row codes fetched by LDS DMA
   __shared__ uint32_t s_ds[kLW * kSlots * 64];  // their scale/bias words
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     s_tag = tag0;
     s_ncand = 0;
   }
+  if (threadIdx.x < kFusedMaxK) s_pick[threadIdx.x] = 0;  // no pick: key 0, expert ~0 = -1
   __syncthreads();
   const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_tag);
 
@@ -337,8 +339,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   //             >= L; those candidates -- a handful for spread-out logits, at most
   //             E -- are appended to an LDS list;
   //         (c) the last wave ranks them: each candidate counts those ahead of it
-  //             (larger key, or equal key and lower index), rank r < K is the r-th
-  //             pick; the picks go to the other waves through LDS.
+  //             (larger key, or equal key and lower index: stored as key << 32 |
+  //             ~index, that is plain u64 order) and the one of rank r < K writes
+  //             itself to pick slot r; the picks go to the other waves through LDS.
   {
     uint64_t lraw[PER_L];
     uint32_t key[PER_L];
@@ -387,45 +390,32 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 #pragma unroll
     for (int j = 0; j < PER_L; ++j)
       if (key[j] != 0 && key[j] >= L) {
-        const uint32_t slot = atomicAdd(&s_ncand, 1u);
-        s_cand[slot] = ((uint64_t)key[j] << 32) | (uint32_t)(threadIdx.x + j * kLB);
+        const uint32_t slot = atomicAdd(&s_ncand, 1u);  // key, then the inverted index:
+        s_cand[slot] = ((uint64_t)key[j] << 32) | ~(uint32_t)(threadIdx.x + j * kLB);  // u64 order
       }
     __syncthreads();
   }
   if (wv == kLW - 1) {
+    // one LDS round trip for the count, this lane's candidate and the first eight
+    // (entries at or past nc are ignored); a candidate of rank r < K is pick r
     const int nc = (int)s_ncand;
-    uint64_t pick[kFusedMaxK];  // key << 32 | expert; expert 0xFFFFFFFF = none
+    uint64_t o[8];
 #pragma unroll
-    for (int r = 0; r < kFusedMaxK; ++r) pick[r] = 0xFFFFFFFFull;
-    // pad the list to a multiple of 8 with zero keys: a zero key is never ahead
-    if (lane < 8) s_cand[nc + lane] = 0;
+    for (int u = 0; u < 8; ++u) o[u] = s_cand[u];
+    const uint64_t cv0 = s_cand[lane];
     for (int c0 = 0; c0 < nc; c0 += 64) {
-      const bool have = c0 + lane < nc;
-      const uint64_t cv = have ? s_cand[c0 + lane] : 0;
-      const uint64_t me = (cv & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)cv);
+      const uint64_t cv = c0 == 0 ? cv0 : s_cand[c0 + lane];
       int rk = 0;
-      for (int c = 0; c < nc; c += 8) {  // eight broadcast reads in flight
-        uint64_t o[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = s_cand[c + u];
+      for (int u = 0; u < 8; ++u) rk += (u < nc && o[u] > cv) ? 1 : 0;
+      for (int c = 8; c < nc; c += 8) {  // more than eight candidates: rare
+        uint64_t o2[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          rk += ((o[u] & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - (uint32_t)o[u])) > me ? 1 : 0;
+        for (int u = 0; u < 8; ++u) o2[u] = s_cand[c + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rk += (c + u < nc && o2[u] > cv) ? 1 : 0;
       }
-#pragma unroll
-      for (int r = 0; r < kFusedMaxK; ++r) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(have && rk == r && r < K);
-        if (m) {
-          const int wl = __builtin_ctzll(m);
-          pick[r] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), wl) << 32) |
-                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv, wl);
-        }
-      }
-    }
-    if (lane < kFusedMaxK) {
-#pragma unroll
-      for (int r = 0; r < kFusedMaxK; ++r)
-        if (lane == r) s_pick[r] = pick[r];
+      if (c0 + lane < nc && rk < K) s_pick[rk] = cv;
     }
   }
   __syncthreads();
@@ -433,8 +423,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   float elog[kFusedMaxK];
 #pragma unroll
   for (int r = 0; r < kFusedMaxK; ++r) {
-    const uint64_t v = r < K ? s_pick[r] : 0xFFFFFFFFull;
-    eidx[r] = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t v = r < K ? s_pick[r] : 0ull;
+    eidx[r] = __builtin_amdgcn_readfirstlane((int)~(uint32_t)v);
     elog[r] = key_value((uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)));
   }
   // renormalised softmax over the K picks (uniform values)
