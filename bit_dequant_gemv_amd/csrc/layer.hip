@@ -11,9 +11,8 @@
 // "rank" = wave * NB + workgroup numbers the waves so that consecutive ranks sit
 // in different workgroups.  Schedule of a workgroup:
 //   1. issue loads: x (staged in LDS; RMS-normalised here when the layer is given
-//      a norm weight), the shared-gate vector, its router rows (4 waves per row),
-//      one shared-expert gate/up row pair per rank below I/RPWH, and (by LDS DMA)
-//      its shared-expert down rows;
+//      a norm weight), the shared-gate vector, its router rows (4 waves per row)
+//      and one shared-expert gate/up row pair per rank below I/RPWH;
 //   2. router dots -> logits (tagged stores);
 //   3. x as fixed-point planes in LDS (once per workgroup);
 //   4. shared gate/up + SwiGLU -> hs (while the other logits are in flight);
@@ -21,9 +20,9 @@
 //      L of the K-th largest logit; the keys >= L go to an LDS list; one wave
 //      ranks them (larger value, then lower index) and passes the picks on;
 //      renormalised softmax of the K selected logits;
-//   6. issue loads: two routed gate/up row pairs per wave;
-//   7. routed gate/up dots + SwiGLU -> hr (tagged); then the routed down rows of
-//      this workgroup (LDS DMA), a wait for everything else, one tagged flag;
+//   6. issue loads: two routed gate/up row pairs per wave, then (into registers)
+//      the wave's shared and routed down rows of this workgroup's output rows;
+//   7. routed gate/up dots + SwiGLU -> hr (tagged); one tagged flag;
 //   8. wait for every workgroup's flag; read hr and hs; their planes; gamma =
 //      sigmoid(g . x); shared and routed down rows; out = residual +
 //      sum_k w_k y_k + gamma y_shared.
@@ -32,11 +31,14 @@
 // device coherence point), so they never need resetting.  The logits are polled
 // word by word.  The h values are read by every workgroup, so polling them would
 // put ~10 MB of coherent reads on a few hundred lines; instead each workgroup,
-// once all its stores are acknowledged, sets one tagged completion flag, and
+// once all its h stores are issued, sets one tagged completion flag, and
 // consumers poll the 256 flags and then read h with ordinary cacheable loads
-// (one fetch per XCD's L2).  A stale cached line shows an old epoch and is
-// re-read coherently; the h buffers rotate over 4 slots so that is rare.  The
-// epoch lives in the workspace: thread 0 of every workgroup reads it before the
+// (one fetch per XCD's L2).  A word with an old epoch (a stale cached line, or a
+// store the flag overtook) is re-read coherently until it carries the current
+// one; the h buffers rotate over 4 slots so that stale lines are rare.  (One
+// shared counter instead of the flags is far slower: device-scope atomics on one
+// word serialise at ~25 ns each.)  The
+// epoch lives in the workspace: every wave of every workgroup reads it before the
 // workgroup's first barrier, every flag is tagged after that barrier, and
 // workgroup 0 advances the epoch once it has seen every flag.  Every wait is
 // bounded; on time-out a status bit is set and the output is undefined (it never
@@ -55,6 +57,10 @@ constexpr int kFusedMaxK = 4;
 constexpr int kFusedMaxE = 2048;
 static_assert(kFusedMaxE % 64 == 0, "the ranking wave reads the candidate list 64 at a time");
 constexpr uint32_t kSpinLimit = 1u << 18;
+// u64 words per 128-byte line: a value written by several CUs into one shared line
+// becomes visible ~0.6 us later than one whose line has a single writer, so the
+// completion flags and each workgroup's pair of logits get a line of their own
+constexpr int kLine = 16;
 constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see step 8
 
 // control words at the start of the workspace
@@ -75,8 +81,8 @@ struct LayerArgs {
   int32_t* idx_out;
   float* w_out;
   uint32_t* ctrl;
-  uint64_t* logits;  // [E]
-  uint64_t* flags;   // [NB]: workgroup b has stored (and seen acknowledged) all its h values
+  uint64_t* logits;  // [E/2][kLine]: logit e is word e % 2 of line e / 2
+  uint64_t* flags;   // [NB][kLine]: workgroup b has issued all its h stores
   uint64_t* hs;      // [kSlotsH][I]
   uint64_t* hr;      // [kSlotsH][K][I]
   int E, K;
@@ -99,31 +105,48 @@ __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Read tagged values after their producers have all signalled completion: na
-// words of a into da and nb words of b into db, every load issued before any is
-// checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32 workgroups
-// of an XCD share one fetch from memory; a word still carrying an old tag comes
-// from a stale cached line (the buffer slot was last used several calls ago) and
-// is re-read coherently.
+// Read tagged values after their producers have all signalled that they issued
+// them: na words of a into da and nb words of b into db, every load issued before
+// any is checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32
+// workgroups of an XCD share one fetch from memory.  A word still carrying an old
+// tag comes from a stale cached line (the buffer slot was last used several calls
+// ago) or from a store not yet visible (a flag may overtake the stores issued
+// before it): those words are re-read coherently, all of them per pass, until they
+// carry the tag (bounded; on time-out ok is cleared).
 template <int PA, int PB>
 __device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uint64_t* b, int nb,
-                                 float* db, uint32_t tag) {
+                                 float* db, uint32_t tag, bool& ok) {
   uint64_t v[PA + PB];
+  uint32_t pending = 0;
 #pragma unroll
   for (int j = 0; j < PA + PB; ++j) {
     const bool in_a = j < PA;
     const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
-    v[j] = i < (in_a ? na : nb) ? (in_a ? a : b)[i] : 0;
+    v[j] = i < (in_a ? na : nb) ? (in_a ? a : b)[i] : ((uint64_t)tag << 32);
+  }
+  for (uint32_t spins = 0;; ++spins) {
+#pragma unroll
+    for (int j = 0; j < PA + PB; ++j)
+      if ((uint32_t)(v[j] >> 32) != tag) pending |= 1u << j;
+      else pending &= ~(1u << j);
+    if (!pending) break;
+    if (spins > kSpinLimit) {
+      ok = false;
+      break;
+    }
+    if (spins) __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < PA + PB; ++j) {
+      const bool in_a = j < PA;
+      const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
+      if ((pending >> j) & 1u) v[j] = tag_get(const_cast<uint64_t*>(in_a ? a : b) + i);
+    }
   }
 #pragma unroll
   for (int j = 0; j < PA + PB; ++j) {
     const bool in_a = j < PA;
     const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
-    if (i < (in_a ? na : nb)) {
-      uint64_t w = v[j];
-      if ((uint32_t)(w >> 32) != tag) w = tag_get(const_cast<uint64_t*>(in_a ? a : b) + i);
-      (in_a ? da : db)[i] = __uint_as_float((uint32_t)w);
-    }
+    if (i < (in_a ? na : nb)) (in_a ? da : db)[i] = __uint_as_float((uint32_t)v[j]);
   }
 }
 
@@ -163,7 +186,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   constexpr int CPLR = (CRQ + 63) / 64;
   constexpr int PW = QTraits<BITS>::PW;
   constexpr int PER_L = (kFusedMaxE + kLB - 1) / kLB;
-  constexpr int kSlots = 1 + MAXR;
 
   const int NB = gridDim.x, wg = blockIdx.x;
   // wave-uniform values go through readfirstlane so that their arithmetic (item,
@@ -191,35 +213,40 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __shared__ uint32_t s_ncand;                 // number of candidates
   __shared__ uint64_t s_cand[kFusedMaxE];      // candidates: key << 32 | ~expert
   __shared__ uint64_t s_pick[kFusedMaxK];      // the picks, in rank order
-  __shared__ uint4 s_dq[kLW * kSlots * 64];     // down-row codes fetched by LDS DMA
-  __shared__ uint32_t s_ds[kLW * kSlots * 64];  // their scale/bias words
   bool ok_all = true;
 
-  uint32_t epoch = 0;
-  if (threadIdx.x == 0)
-    epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // ---- 1. loads: x (once per workgroup, into LDS below) and the shared-gate
-  //         vector, then the router rows, one shared gate/up pair and the shared
-  //         down rows (DMA).  x goes first: vector memory returns in order.
-  uint4 gq = make_uint4(0u, 0u, 0u, 0u);  // shared-gate vector chunk for gamma (step 8)
-  float gx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if ((int)threadIdx.x < H / 8) {
-    const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[0];
-    const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * threadIdx.x)[1];
+  // ---- 1. loads: the epoch, x (once per workgroup, into LDS below), the
+  //         shared-gate vector and the norm weight, then the router rows, one
+  //         shared gate/up pair and the shared down rows (DMA).  Every load here is
+  //         unconditional (clamped addresses; a lane with nothing to load reads a
+  //         valid word it ignores): vector memory completes in issue order, and a
+  //         straight run of loads lets each use below wait for its own data only
+  //         (a conditional load makes the compiler wait for everything).
+  const uint32_t epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int xi = min((int)threadIdx.x, H / 8 - 1);
+  float gx[8], nw[8];
+  uint4 gq;  // shared-gate vector chunk for gamma (step 8)
+  {
+    const float4 f0 = reinterpret_cast<const float4*>(A.x + 8 * xi)[0];
+    const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * xi)[1];
     gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
     gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
-    gq = reinterpret_cast<const uint4*>(A.g)[threadIdx.x];
+    gq = reinterpret_cast<const uint4*>(A.g)[xi];
+    const float* nwp = A.norm_w ? A.norm_w : A.x;  // no norm: a load that is ignored
+    const float4 w0 = reinterpret_cast<const float4*>(nwp + 8 * xi)[0];
+    const float4 w1 = reinterpret_cast<const float4*>(nwp + 8 * xi)[1];
+    nw[0] = w0.x; nw[1] = w0.y; nw[2] = w0.z; nw[3] = w0.w;
+    nw[4] = w1.x; nw[5] = w1.y; nw[6] = w1.z; nw[7] = w1.w;
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the rest
   const int quarter = wv & 3;
   uint4 rq[CPLR];
-  auto router_fetch = [&](int row) {
+  auto router_fetch = [&](int row) {  // a row past E reads row E - 1 (not stored)
+    const int rc = min(row, E - 1);
 #pragma unroll
     for (int i = 0; i < CPLR; ++i) {
-      const int cq = lane + 64 * i;
-      const bool ok = row < E && cq < CRQ;
-      rq[i] = ok ? ld_stream16(A.router + (int64_t)row * H + 8 * (quarter * CRQ + cq))
-                 : make_uint4(0u, 0u, 0u, 0u);
+      const int cq = min(lane + 64 * i, CRQ - 1);
+      rq[i] = ld_stream16(A.router + (int64_t)rc * H + 8 * (quarter * CRQ + cq));
     }
   };
   router_fetch(wg * 2 + (wv >> 2));
@@ -230,34 +257,19 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   uint32_t ssp[2][CPLH];
   RowDot<BITS, LGH, CPLH> dH;
   {
-    const uint8_t* cr[2] = {A.sblk + A.off_g + jsp * RBH, A.sblk + A.off_u + jsp * RBH};
-    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + jsp * GH,
-                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + jsp * GH};
-    const bool ok[2] = {has_sp, has_sp};
-    dH.template fetch<2>(cr, sr, ok, CH, glh, qsp, ssp);
+    const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
+    const uint8_t* cr[2] = {A.sblk + A.off_g + j * RBH, A.sblk + A.off_u + j * RBH};
+    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + j * GH,
+                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + j * GH};
+    dH.template fetch_always<2>(cr, sr, glh, qsp, ssp);
   }
-  // shared-expert down rows of this workgroup: slot 0 of waves 0..DITEMS-1
   const int nl_s = wv * RPWI + subi;
-  const bool sd_ok = wv < DITEMS && nl_s < kRB && row0 + nl_s < H;
-  if (sd_ok) {  // a wave-uniform row base plus a 32-bit lane offset
-    const int sl = wv * kSlots;
-    const int rb = row0 + wv * RPWI;
-    dma16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli),
-          lds_ptr(&s_dq[sl * 64]));
-    dma4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
-             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG),
-         lds_ptr(&s_ds[sl * 64]));
-  }
-  const float resid = (int)threadIdx.x < kRB ? A.residual[row0 + threadIdx.x] : 0.f;
+  const float resid_v = A.residual[row0 + min((int)threadIdx.x, kRB - 1)];
+  const float resid = (int)threadIdx.x < kRB ? resid_v : 0.f;
   if (A.norm_w) {
     // RMSNorm of the input stream, computed by every workgroup: x = h / sqrt(mean(h^2) + eps) * w
-    float nw[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     if ((int)threadIdx.x < H / 8) {
-      const float4 w0 = reinterpret_cast<const float4*>(A.norm_w + 8 * threadIdx.x)[0];
-      const float4 w1 = reinterpret_cast<const float4*>(A.norm_w + 8 * threadIdx.x)[1];
-      nw[0] = w0.x; nw[1] = w0.y; nw[2] = w0.z; nw[3] = w0.w;
-      nw[4] = w1.x; nw[5] = w1.y; nw[6] = w1.z; nw[7] = w1.w;
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(gx[i], gx[i], ss);
     }
@@ -278,13 +290,11 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   }
   __syncthreads();
 
-  // ---- 2. router dots -> logits (the writers, threads 0 and 1, are in the same
-  //         wave as the epoch reader, so the tag needs no barrier)
+  // ---- 2. router dots -> logits (every wave has read the epoch itself)
   // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
   uint32_t tag0 = (uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u;
   tag0 = tag0 ? tag0 : 1u;
-  for (int r0 = wg * 2; r0 < E; r0 += NB * 2) {
-    if (r0 != wg * 2) router_fetch(r0 + (wv >> 2));
+  auto router_rows = [&](int r0) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPLR; ++i) {
@@ -299,11 +309,20 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     acc = group_sum_last<64>(acc);
     if (lane == 63) s_part[wv] = acc;
     __syncthreads();
-    if (threadIdx.x < 2 && r0 + (int)threadIdx.x < E) {
-      const float* pp = s_part + 4 * threadIdx.x;
-      tag_put(A.logits + r0 + threadIdx.x, (pp[0] + pp[1]) + (pp[2] + pp[3]), tag0);
+    if (threadIdx.x < 8) {  // rows r0, r0 + 1 and padding: one whole 64-byte store
+      const bool real = threadIdx.x < 2 && r0 + (int)threadIdx.x < E;
+      const float* pp = s_part + 4 * (threadIdx.x & 1);
+      const float v = real ? (pp[0] + pp[1]) + (pp[2] + pp[3]) : 0.f;
+      tag_put(A.logits + (r0 >> 1) * kLine + threadIdx.x, v, tag0);
     }
     __syncthreads();
+  };
+  // the first pair of rows was fetched in step 1 (outside the loop, so that the
+  // dots wait for those rows only, not for every load issued after them)
+  if (wg * 2 < E) router_rows(wg * 2);
+  for (int r0 = wg * 2 + NB * 2; r0 < E; r0 += NB * 2) {
+    router_fetch(r0 + (wv >> 2));
+    router_rows(r0);
   }
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
@@ -318,6 +337,20 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 
   uint64_t* hs = A.hs + (size_t)(tag % kSlotsH) * I;
   uint64_t* hr = A.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
+  // the first poll of logits 0..kLB-1 (step 5) goes out now, unconditionally (a
+  // lane past E reads logit E - 1), so that its round trip overlaps the shared
+  // gate/up dots; logits from kLB on are first read by the poll loop of step 5
+  uint64_t lraw[PER_L];
+  uint32_t pending = 0;
+  {
+    const int ec = min((int)threadIdx.x, E - 1);
+    lraw[0] = tag_get(A.logits + (ec >> 1) * kLine + (ec & 1));
+  }
+#pragma unroll
+  for (int j = 0; j < PER_L; ++j) {
+    if (j) lraw[j] = 0;  // tag 0 is never current: polled in the loop
+    if ((int)threadIdx.x + j * kLB < E) pending |= 1u << j;
+  }
   dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
   float hs_val = 0.f;
   // ---- 4. shared gate/up + SwiGLU -> hs (one item per wave at most; the logits
@@ -343,19 +376,9 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   //             ~index, that is plain u64 order) and the one of rank r < K writes
   //             itself to pick slot r; the picks go to the other waves through LDS.
   {
-    uint64_t lraw[PER_L];
     uint32_t key[PER_L];
-    uint32_t pending = 0;
 #pragma unroll
-    for (int j = 0; j < PER_L; ++j) {
-      const int e = threadIdx.x + j * kLB;
-      key[j] = 0;
-      lraw[j] = 0;
-      if (e < E) {
-        pending |= 1u << j;
-        lraw[j] = tag_get(A.logits + e);
-      }
-    }
+    for (int j = 0; j < PER_L; ++j) key[j] = 0;
     for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
       for (int j = 0; j < PER_L; ++j)
@@ -371,7 +394,10 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int j = 0; j < PER_L; ++j)
-        if ((pending >> j) & 1u) lraw[j] = tag_get(A.logits + threadIdx.x + j * kLB);
+        if ((pending >> j) & 1u) {
+          const int e = threadIdx.x + j * kLB;
+          lraw[j] = tag_get(A.logits + (e >> 1) * kLine + (e & 1));
+        }
     }
     uint32_t lmax = 0;
 #pragma unroll
@@ -480,57 +506,72 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     // unconditional: a row of a missing expert reads block 0 and is stored as NaN
     dH.template fetch_always<4>(cr, sr, glh, q, sq);
   };
-  if (it < n_rp) fetch_pairs(it);
-  // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step
-  for (; it < n_rp; it += 2 * W) {
-    if (it != rank) fetch_pairs(it);
+  // unconditional, so that the waits below count exactly (a wave without items
+  // reads rows of expert 0 that every such wave shares)
+  fetch_pairs(it);
+  // this wave's down rows of the workgroup's output rows, into registers: its
+  // shared item (waves below DITEMS; another wave reads rows it ignores) and its
+  // MAXR routed items (known since the top-K; an unused one reads a valid row it
+  // ignores).  Issued here, behind the gate/up rows, so that they arrive during
+  // the gate/up dots: loads return in issue order per CU, so loads issued at the
+  // end of step 7 would hold up the flag polls and h reads of step 8.  (The down
+  // rows once went to LDS by DMA; after an LDS DMA the compiler makes the next use
+  // of any loaded register wait for every load, DMA included.)
+  uint4 dq[1 + MAXR];
+  uint32_t dsc[1 + MAXR];
+  {  // wave-uniform row bases plus 32-bit lane offsets
+    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
+    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
+    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
+                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
+  }
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) {
+    const int t = wv * MAXR + m;
+    const int k = t / DITEMS, d = t % DITEMS;
+    const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
+    // every output row of the pass lies inside H (H is a multiple of kRB), so a
+    // valid expert reads rows row0 + d*RPWI + subi
+    const bool ok = (unsigned)e < (unsigned)E;
+    const uint8_t* blk = ok ? A.rbase + (int64_t)e * A.rstride : A.sblk;
+    const int rb = ok ? row0 + d * RPWI : 0;
+    dq[1 + m] = ld_stream16(blk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
+    dsc[1 + m] = ld_stream4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)rb * GI +
+                            (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
+  }
+  // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step (the first
+  //         step outside the loop, so that its dots wait for their own rows only,
+  //         not for the down rows issued after them)
+  auto gate_up_step = [&](int it0) {
     float p[4];
     dH.template dots<4>(q, sq, p);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const float a = group_sum_last<LGH>(p[2 * v]);
       const float u = group_sum_last<LGH>(p[2 * v + 1]);
-      if (group_last<LGH>(lane) && it + v * W < n_rp)
+      if (group_last<LGH>(lane) && it0 + v * W < n_rp)
         tag_put(hr + kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
     }
+  };
+  if (it < n_rp) gate_up_step(it);
+  for (it += 2 * W; it < n_rp; it += 2 * W) {
+    fetch_pairs(it);
+    gate_up_step(it);
   }
-  // ---- 7b. the routed down rows of this workgroup's output rows (LDS DMA, slots
-  //          1..MAXR), issued only now: they are needed after the h hand-off, not
-  //          before it, so they stay out of the way of the gate/up rows.  Every
-  //          wave issues exactly 2*MAXR DMA instructions (an unused slot reads a
-  //          valid row it then ignores), so the wait below can leave them in flight.
-#pragma unroll
-  for (int m = 0; m < MAXR; ++m) {
-    const int t = wv * MAXR + m;
-    const int k = t / DITEMS, d = t % DITEMS;
-    const int e = (t < K * DITEMS && k < kFusedMaxK) ? eidx[k] : -1;
-    // wave-uniform choices: every output row of the pass lies inside H (H is a
-    // multiple of kRB), so a valid expert reads rows row0 + d*RPWI + subi
-    const bool ok = (unsigned)e < (unsigned)E;
-    const uint8_t* blk = ok ? A.rbase + (int64_t)e * A.rstride : A.sblk;
-    const int rb = ok ? row0 + d * RPWI : 0;
-    const int sl = wv * kSlots + 1 + m;
-    dma16(blk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli),
-          lds_ptr(&s_dq[sl * 64]));
-    dma4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)rb * GI +
-             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG),
-         lds_ptr(&s_ds[sl * 64]));
-  }
-  // completion: every store of this workgroup acknowledged (all vector memory
-  // operations but the 2*MAXR DMA just issued), then one tagged flag
-  // (a bare barrier: it only orders the acknowledged stores of every wave before
-  // the flag; no LDS is handed over here, and a fence would wait for the DMA)
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * MAXR));
+  // completion: once every wave has issued its h stores, one tagged flag, written
+  // as a whole 64-byte store into a line of its own.  A bare barrier: it orders
+  // the issue only.  Waiting for the stores' acknowledgement first would cost
+  // ~0.5 us here; the flag may instead become visible before some of them, and
+  // the reader re-reads any word that still has an old tag.
   __builtin_amdgcn_s_barrier();
-  if (threadIdx.x == 0) tag_put(A.flags + wg, 0.f, tag);
-
+  if (threadIdx.x < 8) tag_put(A.flags + wg * kLine + threadIdx.x, 0.f, tag);
   // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
-  //         routed down rows (integer dots against the planes of h, codes from the
-  //         LDS DMA);
+  //         routed down rows (integer dots against the planes of h, codes in
+  //         registers since step 6);
   //         combine
   if ((int)threadIdx.x < NB) {
     uint32_t spins = 0;
-    while ((uint32_t)(tag_get(A.flags + threadIdx.x) >> 32) != tag) {
+    while ((uint32_t)(tag_get(A.flags + threadIdx.x * kLine) >> 32) != tag) {
       if (++spins > kSpinLimit) {
         ok_all = false;
         break;
@@ -543,19 +584,19 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   if (wg == 0 && threadIdx.x == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
-      hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag);
+      hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag, ok_all);
   __syncthreads();
   // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
   // two vectors; unused routed slots hold stale values whose planes are not read)
   prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, threadIdx.x, kLB);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA (steps 1 and 7) has landed
   __syncthreads();
-  const float gpart = group_sum_last<64>(bf16_chunk_dot(gq, gx));
+  // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
+  const float gpart = group_sum_last<64>((int)threadIdx.x < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
   if (lane == 63) s_rv[wv] = gpart;
   // down rows: the wave's shared item (waves below DITEMS) and its MAXR routed
   // items, which all belong to one expert kw, as one branch-free block so that
-  // their LDS reads, dots and reductions interleave; a slot without a row holds
-  // codes that are read and then ignored
+  // their plane reads, dots and reductions interleave; an item without a row holds
+  // codes that are used and then ignored
   static_assert(DITEMS % MAXR == 0, "the routed down items of a wave share one expert");
   const int kw = (wv * MAXR) / DITEMS;
   if (wv < DITEMS || kw < K) {
@@ -564,14 +605,14 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     dS.load_prepped(s_hp + kFusedMaxK * CI * PW, s_hsc + kFusedMaxK * CI, s_hsum + kFusedMaxK * CI,
                     CI, gli);
     dR.load_prepped(s_hp + kr * CI * PW, s_hsc + kr * CI, s_hsum + kr * CI, CI, gli);
-    const uint4 qs[1][1] = {{s_dq[wv * kSlots * 64 + lane]}};
-    const uint32_t ss[1][1] = {{s_ds[wv * kSlots * 64 + lane]}};
+    const uint4 qs[1][1] = {{dq[0]}};
+    const uint32_t ss[1][1] = {{dsc[0]}};
     uint4 qr[MAXR][1];
     uint32_t sr[MAXR][1];
 #pragma unroll
     for (int m = 0; m < MAXR; ++m) {
-      qr[m][0] = s_dq[(wv * kSlots + 1 + m) * 64 + lane];
-      sr[m][0] = s_ds[(wv * kSlots + 1 + m) * 64 + lane];
+      qr[m][0] = dq[1 + m];
+      sr[m][0] = dsc[1 + m];
     }
     float ps[1], pr[MAXR];
     dS.template dots<1>(qs, ss, ps);
@@ -623,8 +664,8 @@ WsLayout fused_ws(int E, int H, int I) {
   WsLayout w;
   w.ctrl = 0;
   w.logits = 256;
-  w.flags = w.logits + align256((int64_t)E * 8);
-  w.hs = w.flags + align256((int64_t)(H / kRB) * 8);
+  w.flags = w.logits + align256((int64_t)((E + 1) / 2) * kLine * 8);
+  w.hs = w.flags + align256((int64_t)(H / kRB) * kLine * 8);
   w.hr = w.hs + align256((int64_t)kSlotsH * I * 8);
   w.total = w.hr + align256((int64_t)kSlotsH * kFusedMaxK * I * 8);
   return w;
@@ -675,6 +716,7 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
+  if (H / kRB > kLB / 2) return c;  // the flag pollers are the waves without down-row DMA
   const int cus = device_cus();
   if (cus <= 0) return c;
   int blocks_per_cu = 0;
