@@ -11,8 +11,9 @@
 // "rank" = wave * NB + workgroup numbers the waves so that consecutive ranks sit
 // in different workgroups.  Schedule of a workgroup:
 //   1. issue loads: x (staged in LDS; RMS-normalised here when the layer is given
-//      a norm weight), the shared-gate vector, its router rows (4 waves per row)
-//      and one shared-expert gate/up row pair per rank below I/RPWH;
+//      a norm weight), the shared-gate vector, its router rows (4 waves per row),
+//      one shared-expert gate/up row pair per rank below I/RPWH and (into
+//      registers) the wave's shared-expert down rows;
 //   2. router dots -> logits (tagged stores);
 //   3. x as fixed-point planes in LDS (once per workgroup);
 //   4. shared gate/up + SwiGLU -> hs (while the other logits are in flight);
@@ -21,7 +22,7 @@
 //      ranks them (larger value, then lower index) and passes the picks on;
 //      renormalised softmax of the K selected logits;
 //   6. issue loads: two routed gate/up row pairs per wave, then (into registers)
-//      the wave's shared and routed down rows of this workgroup's output rows;
+//      the wave's routed down rows of this workgroup's output rows;
 //   7. routed gate/up dots + SwiGLU -> hr (tagged); one tagged flag;
 //   8. wait for every workgroup's flag; read hr and hs; their planes; gamma =
 //      sigmoid(g . x); shared and routed down rows; out = residual +
@@ -264,6 +265,16 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     dH.template fetch_always<2>(cr, sr, glh, qsp, ssp);
   }
   const int nl_s = wv * RPWI + subi;
+  // this wave's shared down item (waves below DITEMS; another wave reads rows it
+  // ignores), into registers: HBM is otherwise idle during the top-K
+  uint4 dq[1 + MAXR];
+  uint32_t dsc[1 + MAXR];
+  {  // a wave-uniform row base plus a 32-bit lane offset
+    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
+    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
+    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
+                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
+  }
   const float resid_v = A.residual[row0 + min((int)threadIdx.x, kRB - 1)];
   const float resid = (int)threadIdx.x < kRB ? resid_v : 0.f;
   if (A.norm_w) {
@@ -509,22 +520,13 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // unconditional, so that the waits below count exactly (a wave without items
   // reads rows of expert 0 that every such wave shares)
   fetch_pairs(it);
-  // this wave's down rows of the workgroup's output rows, into registers: its
-  // shared item (waves below DITEMS; another wave reads rows it ignores) and its
-  // MAXR routed items (known since the top-K; an unused one reads a valid row it
+  // this wave's routed down rows of the workgroup's output rows, into registers:
+  // MAXR items (known since the top-K; an unused one reads a valid row it
   // ignores).  Issued here, behind the gate/up rows, so that they arrive during
   // the gate/up dots: loads return in issue order per CU, so loads issued at the
   // end of step 7 would hold up the flag polls and h reads of step 8.  (The down
   // rows once went to LDS by DMA; after an LDS DMA the compiler makes the next use
   // of any loaded register wait for every load, DMA included.)
-  uint4 dq[1 + MAXR];
-  uint32_t dsc[1 + MAXR];
-  {  // wave-uniform row bases plus 32-bit lane offsets
-    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
-    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
-    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
-                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
-  }
 #pragma unroll
   for (int m = 0; m < MAXR; ++m) {
     const int t = wv * MAXR + m;
