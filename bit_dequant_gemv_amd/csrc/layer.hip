@@ -252,29 +252,6 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   };
   router_fetch(wg * 2 + (wv >> 2));
 
-  const bool has_sp = rank < NSP;
-  const int jsp = rank * RPWH + subh;
-  uint4 qsp[2][CPLH];
-  uint32_t ssp[2][CPLH];
-  RowDot<BITS, LGH, CPLH> dH;
-  {
-    const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
-    const uint8_t* cr[2] = {A.sblk + A.off_g + j * RBH, A.sblk + A.off_u + j * RBH};
-    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + j * GH,
-                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + j * GH};
-    dH.template fetch_always<2>(cr, sr, glh, qsp, ssp);
-  }
-  const int nl_s = wv * RPWI + subi;
-  // this wave's shared down item (waves below DITEMS; another wave reads rows it
-  // ignores), into registers: HBM is otherwise idle during the top-K
-  uint4 dq[1 + MAXR];
-  uint32_t dsc[1 + MAXR];
-  {  // a wave-uniform row base plus a 32-bit lane offset
-    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
-    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
-    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
-                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
-  }
   const float resid_v = A.residual[row0 + min((int)threadIdx.x, kRB - 1)];
   const float resid = (int)threadIdx.x < kRB ? resid_v : 0.f;
   if (A.norm_w) {
@@ -334,6 +311,31 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   for (int r0 = wg * 2 + NB * 2; r0 < E; r0 += NB * 2) {
     router_fetch(r0 + (wv >> 2));
     router_rows(r0);
+  }
+  // the shared expert's loads go out only now: in step 1 they would share the
+  // start-up burst with the router rows, whose logits everything else waits for
+  const bool has_sp = rank < NSP;
+  const int jsp = rank * RPWH + subh;
+  uint4 qsp[2][CPLH];
+  uint32_t ssp[2][CPLH];
+  RowDot<BITS, LGH, CPLH> dH;
+  {
+    const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
+    const uint8_t* cr[2] = {A.sblk + A.off_g + j * RBH, A.sblk + A.off_u + j * RBH};
+    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + j * GH,
+                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + j * GH};
+    dH.template fetch_always<2>(cr, sr, glh, qsp, ssp);
+  }
+  const int nl_s = wv * RPWI + subi;
+  // this wave's shared down item (waves below DITEMS; another wave reads rows it
+  // ignores), into registers: HBM would otherwise idle during the top-K
+  uint4 dq[1 + MAXR];
+  uint32_t dsc[1 + MAXR];
+  {  // a wave-uniform row base plus a 32-bit lane offset
+    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
+    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
+    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
+                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
   }
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
