@@ -43,6 +43,48 @@ inline size_t prep_lds_bytes(int n) {
   return (size_t)C * (QTraits<BITS>::PW + 2) * 4;
 }
 
+// The input vector of an expert FFN kernel, with the weight rows' loads issued in
+// between (fetch): the n inputs are loaded into registers first, unconditionally
+// (kXW words of 8 per thread, a thread past the end reading the last word again),
+// then the rows; then the inputs are staged in dynamic LDS after the planes and
+// the planes are built there while the rows are still on their way, and each lane
+// takes its chunks' planes.  Vector memory completes in issue order, and a
+// straight run of loads lets each use wait for its own data only.
+constexpr int kXW = 4;  // words per thread: n <= 8 * kXW * kBlock = 8192 inputs
+template <int BITS, int LG, int CPL, typename Fetch>
+__device__ __forceinline__ void x_planes_around(RowDot<BITS, LG, CPL>& rd, const float* x, int n,
+                                                int C, int gl, Fetch fetch) {
+  extern __shared__ uint32_t smem[];
+  const int words = n / 8;
+  float4 xr[2 * kXW];
+#pragma unroll
+  for (int k = 0; k < kXW; ++k) {
+    const int w = min((int)threadIdx.x + k * kBlock, words - 1);
+    xr[2 * k] = reinterpret_cast<const float4*>(x + 8 * w)[0];
+    xr[2 * k + 1] = reinterpret_cast<const float4*>(x + 8 * w)[1];
+  }
+  fetch();  // (a scheduling barrier here would push xr to scratch memory)
+  uint32_t* planes = smem;
+  float* scl = reinterpret_cast<float*>(smem + C * QTraits<BITS>::PW);
+  float* xsum = scl + C;
+  float* xs = xsum + C;  // staged inputs
+#pragma unroll
+  for (int k = 0; k < kXW; ++k) {  // a clamped thread writes the last word again, unchanged
+    const int w = min((int)threadIdx.x + k * kBlock, words - 1);
+    reinterpret_cast<float4*>(xs + 8 * w)[0] = xr[2 * k];
+    reinterpret_cast<float4*>(xs + 8 * w)[1] = xr[2 * k + 1];
+  }
+  __syncthreads();
+  prep_x_coop<BITS>(xs, n, planes, scl, xsum, threadIdx.x, blockDim.x);
+  __syncthreads();
+  rd.load_prepped(planes, scl, xsum, C, gl);
+}
+
+template <int BITS>
+inline size_t ffn_lds_bytes(int n) {
+  return prep_lds_bytes<BITS>(n) + (size_t)n * 4;
+}
+
 // ---------------------------------------------------------------------------
 // y = W x
 // A persistent grid (a few workgroups per CU) walks the rows; each wave keeps the
@@ -162,7 +204,7 @@ inline PoolArgs pool_args(const qmoe_expert_pool& p) {
 // grid.y = expert slot; x of slot i at x + i*x_stride; h[i][I] written
 template <int BITS, int LG, int CPL, int R>
 __global__ __launch_bounds__(kBlock) void k_ffn_gateup(PoolArgs P, const int32_t* __restrict__ idx,
-                                                       const float* __restrict__ x,
+                                                       const float* x,  // not restrict: see x_planes_around
                                                        int64_t x_stride, float* __restrict__ h) {
   constexpr int RPW = 64 / LG;
   const int slot = blockIdx.y;
@@ -179,25 +221,28 @@ __global__ __launch_bounds__(kBlock) void k_ffn_gateup(PoolArgs P, const int32_t
   const int lane = threadIdx.x & 63;
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
-  load_x_shared<BITS, LG, CPL>(rd, x + slot * x_stride, P.H, C, gl);
-  const int nw = gridDim.x * (kBlock / 64);
-  for (int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R; base < P.I;
-       base += nw * RPW * R) {
+  // a pass's rows, unconditionally (a row past the end reads the last one)
+  auto fetch = [&](int base, uint4 (&q)[2 * R][CPL], uint32_t (&s)[2 * R][CPL]) {
     const uint8_t* crow[2 * R];
     const uint32_t* srow[2 * R];
-    bool ok[2 * R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int j = base + r * RPW + sub;
-      ok[2 * r] = ok[2 * r + 1] = eok && j < P.I;
+      const int j = min(base + r * RPW + sub, P.I - 1);
       crow[2 * r] = gc + j * rowbytes;
       crow[2 * r + 1] = uc + j * rowbytes;
       srow[2 * r] = gs + (int64_t)j * G;
       srow[2 * r + 1] = us + (int64_t)j * G;
     }
-    uint4 q[2 * R][CPL];
-    uint32_t s[2 * R][CPL];
-    rd.template fetch<2 * R>(crow, srow, ok, C, gl, q, s);
+    rd.template fetch_clamped<2 * R>(crow, srow, C, gl, q, s);
+  };
+  const int nw = gridDim.x * (kBlock / 64);
+  int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
+  uint4 q[2 * R][CPL];
+  uint32_t s[2 * R][CPL];
+  // the first pass's rows go out between the loads and the planes of x
+  x_planes_around<BITS, LG, CPL>(rd, x + slot * x_stride, P.H, C, gl, [&] { fetch(base, q, s); });
+  for (bool first = true; base < P.I; base += nw * RPW * R, first = false) {
+    if (!first) fetch(base, q, s);
     float p[2 * R];
     rd.template dots<2 * R>(q, s, p);
 #pragma unroll
@@ -213,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void k_ffn_gateup(PoolArgs P, const int32_t
 // grid.y = expert slot; input h[slot], output y[slot][H]
 template <int BITS, int LG, int CPL, int R>
 __global__ __launch_bounds__(kBlock) void k_ffn_down(PoolArgs P, const int32_t* __restrict__ idx,
-                                                     const float* __restrict__ h,
+                                                     const float* h,  // not restrict: see x_planes_around
                                                      float* __restrict__ y) {
   constexpr int RPW = 64 / LG;
   const int slot = blockIdx.y;
@@ -228,23 +273,25 @@ __global__ __launch_bounds__(kBlock) void k_ffn_down(PoolArgs P, const int32_t* 
   const int lane = threadIdx.x & 63;
   const int gl = lane % LG, sub = lane / LG;
   RowDot<BITS, LG, CPL> rd;
-  load_x_shared<BITS, LG, CPL>(rd, h + (int64_t)slot * P.I, P.I, C, gl);
-  const int nw = gridDim.x * (kBlock / 64);
-  for (int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R; base < P.H;
-       base += nw * RPW * R) {
+  auto fetch = [&](int base, uint4 (&q)[R][CPL], uint32_t (&s)[R][CPL]) {
     const uint8_t* crow[R];
     const uint32_t* srow[R];
-    bool ok[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = base + r * RPW + sub;
-      ok[r] = eok && n < P.H;
+      const int n = min(base + r * RPW + sub, P.H - 1);
       crow[r] = dc + n * rowbytes;
       srow[r] = ds + (int64_t)n * G;
     }
-    uint4 q[R][CPL];
-    uint32_t s[R][CPL];
-    rd.template fetch<R>(crow, srow, ok, C, gl, q, s);
+    rd.template fetch_clamped<R>(crow, srow, C, gl, q, s);
+  };
+  const int nw = gridDim.x * (kBlock / 64);
+  int base = (blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * RPW * R;
+  uint4 q[R][CPL];
+  uint32_t s[R][CPL];
+  // the first pass's rows go out between the loads and the planes of h
+  x_planes_around<BITS, LG, CPL>(rd, h + (int64_t)slot * P.I, P.I, C, gl, [&] { fetch(base, q, s); });
+  for (bool first = true; base < P.H; base += nw * RPW * R, first = false) {
+    if (!first) fetch(base, q, s);
     float p[R];
     rd.template dots<R>(q, s, p);
 #pragma unroll
@@ -262,7 +309,7 @@ hipError_t run_gateup(const PoolArgs& P, const int32_t* idx, int n, const float*
   constexpr int R = RowsPerPass<CPL>::R > 1 ? RowsPerPass<CPL>::R / 2 : 1;
   const int waves = ceil_div(P.I, (64 / LG) * R);
   hipLaunchKernelGGL((k_ffn_gateup<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock),
-                     prep_lds_bytes<BITS>(P.H), s, P, idx, x, x_stride, h);
+                     ffn_lds_bytes<BITS>(P.H), s, P, idx, x, x_stride, h);
   return hipGetLastError();
 }
 
@@ -272,7 +319,7 @@ hipError_t run_down(const PoolArgs& P, const int32_t* idx, int n, const float* h
   constexpr int R = RowsPerPass<CPL>::R;
   const int waves = ceil_div(P.H, (64 / LG) * R);
   hipLaunchKernelGGL((k_ffn_down<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock),
-                     prep_lds_bytes<BITS>(P.I), s, P, idx, h, y);
+                     ffn_lds_bytes<BITS>(P.I), s, P, idx, h, y);
   return hipGetLastError();
 }
 
