@@ -36,7 +36,9 @@ struct BatchWs {
   // grp block: n_groups | group_expert[GM] | group_off[GM+1] | pair_list[T*K+T]
 };
 
-inline int max_groups(int T, int K) { return T * K + T; }  // every chunk holds >= 1 pair
+// group chunks in all, at most: a routed expert's chunks hold >= 1 pair each
+// (<= T*K of them), the shared expert's ceil(T / kChunk)
+inline int max_groups(int T, int K) { return T * K + (T + kChunk - 1) / kChunk; }
 
 BatchWs batch_ws(int E, int K, int H, int I, int T, int bits) {
   BatchWs b;
