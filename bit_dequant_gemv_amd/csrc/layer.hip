@@ -11,10 +11,11 @@
 // "rank" = wave * NB + workgroup numbers the waves so that consecutive ranks sit
 // in different workgroups.  Schedule of a workgroup:
 //   1. issue loads: x (staged in LDS; RMS-normalised here when the layer is given
-//      a norm weight), the shared-gate vector, its router rows (4 waves per row),
-//      one shared-expert gate/up row pair per rank below I/RPWH and (into
-//      registers) the wave's shared-expert down rows;
-//   2. router dots -> logits (tagged stores);
+//      a norm weight), the shared-gate vector and its router rows (4 waves per
+//      row);
+//   2. router dots -> logits (tagged stores); then issue the shared expert's
+//      loads: one gate/up row pair per rank below I/RPWH and (into registers) the
+//      wave's shared down rows;
 //   3. x as fixed-point planes in LDS (once per workgroup);
 //   4. shared gate/up + SwiGLU -> hs (while the other logits are in flight);
 //   5. top-K: every thread polls its logits; from the 8 wave maxima a lower bound
@@ -97,10 +98,6 @@ __device__ __forceinline__ void tag_put(uint64_t* p, float v, uint32_t tag) {
 __device__ __forceinline__ uint64_t tag_get(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// s_waitcnt immediate that waits until at most n vector memory operations are
-// outstanding (expcnt and lgkmcnt left at their maxima; gfx9 field layout)
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -217,12 +214,12 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   bool ok_all = true;
 
   // ---- 1. loads: the epoch, x (once per workgroup, into LDS below), the
-  //         shared-gate vector and the norm weight, then the router rows, one
-  //         shared gate/up pair and the shared down rows (DMA).  Every load here is
-  //         unconditional (clamped addresses; a lane with nothing to load reads a
-  //         valid word it ignores): vector memory completes in issue order, and a
-  //         straight run of loads lets each use below wait for its own data only
-  //         (a conditional load makes the compiler wait for everything).
+  //         shared-gate vector and the norm weight, then the router rows.  Every
+  //         load of the kernel's straight-line parts is unconditional (clamped
+  //         addresses; a lane with nothing to load reads a valid word it ignores):
+  //         vector memory completes in issue order, and a straight run of loads
+  //         lets each use below wait for its own data only (a conditional load
+  //         makes the compiler wait for everything).
   const uint32_t epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int xi = min((int)threadIdx.x, H / 8 - 1);
   float gx[8], nw[8];
@@ -720,7 +717,7 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
-  if (H / kRB > kLB / 2) return c;  // the flag pollers are the waves without down-row DMA
+  if (H / kRB > kLB) return c;  // every completion flag needs a polling thread
   const int cus = device_cus();
   if (cus <= 0) return c;
   int blocks_per_cu = 0;

@@ -453,24 +453,6 @@ __device__ __forceinline__ uint32_t ld_stream4(const uint32_t* p) {
   return __builtin_nontemporal_load(p);
 }
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-template <typename T>
-__device__ __forceinline__ lds_void_ptr lds_ptr(T* p) {
-  return (lds_void_ptr)(p);
-}
-
-// LDS DMA (global_load_lds): lane l's 16 (or 4) bytes land at lds + 16*l (4*l),
-// with the non-temporal cache policy (cache-policy bit 1) like every weight load.
-// Kept in plain device functions: calling the builtin directly inside the kernel
-// template makes the host-side kernel handle go missing.
-constexpr int kCpolNT = 2;
-__device__ __forceinline__ void dma16(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, kCpolNT);
-}
-__device__ __forceinline__ void dma4(const void* g, lds_void_ptr lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, kCpolNT);
-}
-
 // A lane's slice of x (as fixed-point planes) for one matrix, and the row dots.
 template <int BITS, int LG, int CPL>
 struct RowDot {
