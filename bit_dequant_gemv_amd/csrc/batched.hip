@@ -234,12 +234,19 @@ __global__ __launch_bounds__(kBB) void k_bgateup(PoolArgsB P, GroupTables G,
   uint4 q[2 * NR][CPL];
   uint32_t s[2 * NR][CPL];
   rd.template fetch<2 * NR>(cr, sr, ok, C, gl, q, s);
-  for (int pi = p0; pi < p1; ++pi) {
-    const int p = G.pair_list[pi];
-    const int t = token_of(p, P.T, P.K);
+  // the first token's planes go out right behind the rows, before anything waits
+  // for them, so that both arrive in one round trip
+  auto planes_of = [&](int pi) {
+    const int t = token_of(G.pair_list[pi], P.T, P.K);
     const uint32_t* planes = xp + (int64_t)t * pw;
     const float* scl = reinterpret_cast<const float*>(planes + C * QTraits<BITS>::PW);
     rd.load_prepped(planes, scl, scl + C, C, gl);
+  };
+  if (p0 < p1) planes_of(p0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int pi = p0; pi < p1; ++pi) {
+    const int p = G.pair_list[pi];
+    if (pi != p0) planes_of(pi);
     float pp[2 * NR];
     rd.template dots<2 * NR>(q, s, pp);
 #pragma unroll
@@ -286,11 +293,17 @@ __global__ __launch_bounds__(kBB) void k_bdown(PoolArgsB P, GroupTables G,
   uint4 q[NR][CPL];
   uint32_t s[NR][CPL];
   rd.template fetch<NR>(cr, sr, ok, C, gl, q, s);
-  for (int pi = p0; pi < p1; ++pi) {
-    const int p = G.pair_list[pi];
-    const uint32_t* planes = hp + (int64_t)p * pw;
+  // the first pair's planes go out right behind the rows (as in k_bgateup)
+  auto planes_of = [&](int pi) {
+    const uint32_t* planes = hp + (int64_t)G.pair_list[pi] * pw;
     const float* scl = reinterpret_cast<const float*>(planes + C * QTraits<BITS>::PW);
     rd.load_prepped(planes, scl, scl + C, C, gl);
+  };
+  if (p0 < p1) planes_of(p0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int pi = p0; pi < p1; ++pi) {
+    const int p = G.pair_list[pi];
+    if (pi != p0) planes_of(pi);
     float pp[NR];
     rd.template dots<NR>(q, s, pp);
 #pragma unroll
