@@ -316,7 +316,9 @@ hipError_t run_gateup(const PoolArgs& P, const int32_t* idx, int n, const float*
 template <int BITS, int LG, int CPL>
 hipError_t run_down(const PoolArgs& P, const int32_t* idx, int n, const float* h, float* y,
                     hipStream_t s) {
-  constexpr int R = RowsPerPass<CPL>::R;
+  // half the rows per pass of the stand-alone GEMV: twice the workgroups, every
+  // CU busy for one expert (measured: 8.59 -> 8.22 us per expert FFN call)
+  constexpr int R = RowsPerPass<CPL>::R > 1 ? RowsPerPass<CPL>::R / 2 : 1;
   const int waves = ceil_div(P.H, (64 / LG) * R);
   hipLaunchKernelGGL((k_ffn_down<BITS, LG, CPL, R>), dim3(ceil_div(waves, 4), n), dim3(kBlock),
                      ffn_lds_bytes<BITS>(P.I), s, P, idx, h, y);
