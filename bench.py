@@ -358,26 +358,27 @@ def run_stack_bench(args, torch, q, synth):
         norm.append(w)
     H0 = make_x_ring(torch, synth, seed, n_tok)
     h = torch.empty(H, dtype=torch.float32, device="cuda")
-    idx = torch.empty(K, dtype=torch.int32, device="cuda")
-    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    idx = torch.empty(n_layers, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(n_layers, K, dtype=torch.float32, device="cuda")
+    S = q.Stack([W.L for W in layers], norm)
+    ws = q.alloc_stack_workspace(S)
 
-    def token(t):
-        h.copy_(H0[t])
-        for l in range(n_layers):  # one launch per layer: h <- h + MoE(rmsnorm(h))
-            q.moe_layer_forward_norm(layers[l].L, h, norm[l], 1e-6, h, idx, w, layers[l].ws)
+    def token(t):  # h <- h + MoE_l(rmsnorm(h)) for the 60 layers
+        q.moe_stack_forward(S, H0[t], 1e-6, out=h, idx=idx, w=w, ws=ws, persistent=args.persistent)
 
     calls = [(lambda t=t: token(t)) for t in range(n_tok)]
     steps = max(1, min(args.steps, 4096))
     dt = timed_steps(torch, calls, steps, args.warmup, 8)
-    for W in layers[:1]:
-        if int(W.ws[4:8].view(torch.int32).item()) != 0:
+    for wsp in [ws]:
+        if int(wsp[4:8].view(torch.int32).item()) != 0:
             raise RuntimeError("fused layer kernel reported a time-out")
     per_tok = n_layers * (layer_bytes(4) + H * 4)  # + the RMSNorm weight
     tok_s = steps / dt
     roof = {"bound": "hbm", "achieved": round(per_tok * tok_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": None}
-    extra = {"kernel": "k_layer x60 per token, RMSNorm fused (roofline over the token)",
+    kern = ("k_stack, 32 + 28 layers per launch" if args.persistent else "k_layer x60 per token")
+    extra = {"kernel": kern + ", RMSNorm fused (roofline over the token)",
              "bytes_per_token": per_tok, "layer_evals_per_s": round(tok_s * n_layers, 1),
              "resident_GB": round(sum(W.routed.buf.numel() + W.shared.buf.numel() for W in layers) / 1e9, 1)}
     cpu = None
@@ -463,6 +464,9 @@ def main():
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--persistent", action="store_true",
+                    help="config 3: the persistent stack kernel (32 layers per launch) instead of "
+                         "one fused launch per layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "

@@ -72,6 +72,9 @@ _SIGS = {
     "moe_layer_forward_batched": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
                                    _vp], ctypes.c_int),
     "qmoe_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
+    "moe_stack_forward": ([ctypes.POINTER(LayerC), ctypes.POINTER(_vp), _i32, _f32, _vp, _vp, _vp, _vp,
+                           _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
+    "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
     "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
     "qmoe_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "qmoe_last_error": ([], ctypes.c_char_p),
@@ -267,6 +270,56 @@ def moe_layer_forward_norm(layer: Layer, h, norm_w, eps=1e-6, out=None, idx=None
                                        _ptr(out, torch.float32, "out"), _ptr(idx, torch.int32, "idx"),
                                        _ptr(w, torch.float32, "w"), _ptr(ws, None, "ws"), ws.numel(),
                                        _stream()), "moe_layer_forward_norm")
+    return out, idx, w
+
+
+class Stack:
+    """Layers of one shape with their RMSNorm weights, marshalled once for
+    moe_stack_forward (the C structs and the pointer table live as long as this)."""
+
+    def __init__(self, layers, norm_ws):
+        if len(layers) != len(norm_ws) or not layers:
+            raise ValueError("one RMSNorm weight per layer, at least one layer")
+        self.layers, self.norm_ws = list(layers), list(norm_ws)
+        self.n = len(self.layers)
+        self.top_k = self.layers[0].top_k
+        self._lc = (LayerC * self.n)(*[L.c() for L in self.layers])
+        self._nw = (_vp * self.n)(*[_ptr(w, torch.float32, "norm_w").value for w in self.norm_ws])
+
+
+def qmoe_stack_workspace_bytes(stack: Stack) -> int:
+    return int(_lib.qmoe_stack_workspace_bytes(stack._lc, stack.n))
+
+
+def alloc_stack_workspace(stack: Stack) -> torch.Tensor:
+    """A zero-filled workspace for moe_stack_forward (it also serves moe_layer_forward)."""
+    n = qmoe_stack_workspace_bytes(stack)
+    if n == 0:
+        raise ValueError("bad stack")
+    return torch.zeros(n, dtype=torch.uint8, device=stack.layers[0].routed.buf.device)
+
+
+QMOE_STACK_PERSISTENT = 1
+
+
+def moe_stack_forward(stack: Stack, h0, eps=1e-6, out=None, h_all=None, idx=None, w=None, ws=None,
+                      persistent=False):
+    """h <- h + MoE_l(rmsnorm(h, norm_w[l])) through every layer of the stack: one
+    fused launch per layer, or (persistent) one launch per 32 layers.  Returns
+    (out [H], idx int32 [n, K], w [n, K]).  h_all: a float tensor [n, H] that
+    receives every layer's output, or None."""
+    dev = h0.device
+    out = out if out is not None else torch.empty_like(h0)
+    idx = idx if idx is not None else torch.empty(stack.n, stack.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(stack.n, stack.top_k, dtype=torch.float32, device=dev)
+    if ws is None:
+        raise ValueError("pass a persistent workspace from alloc_stack_workspace(stack)")
+    ha = None if h_all is None else _ptr(h_all, torch.float32, "h_all")
+    _check(_lib.moe_stack_forward(stack._lc, stack._nw, stack.n, eps, _ptr(h0, torch.float32, "h0"),
+                                  _ptr(out, torch.float32, "out"), ha, _ptr(idx, torch.int32, "idx"),
+                                  _ptr(w, torch.float32, "w"), QMOE_STACK_PERSISTENT if persistent else 0,
+                                  _ptr(ws, None, "ws"), ws.numel(), _stream()),
+           "moe_stack_forward")
     return out, idx, w
 
 

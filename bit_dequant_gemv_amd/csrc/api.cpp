@@ -245,6 +245,43 @@ int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* nor
                     "moe_layer_forward_norm launch");
 }
 
+size_t qmoe_stack_workspace_bytes(const qmoe_layer* layers, int32_t n_layers) {
+  if (!layers || n_layers < 1) return 0;
+  return qmoe::stack_workspace_bytes(layers[0], n_layers);
+}
+
+int moe_stack_forward(const qmoe_layer* layers, const float* const* norm_w, int32_t n_layers,
+                      float eps, const float* h0, float* out, float* h_all, int32_t* topk_idx,
+                      float* topk_w, int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || !norm_w) return fail(QMOE_EINVAL, "layers or norm_w is NULL");
+  if (flags & ~QMOE_STACK_PERSISTENT) return fail(QMOE_EINVAL, "unknown flags 0x%x", flags);
+  if (n_layers < 1) return fail(QMOE_EINVAL, "n_layers must be >= 1");
+  const qmoe_layer& L0 = layers[0];
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = check_layer(&layers[l]);
+    if (rc) return rc;
+    const qmoe_layer& L = layers[l];
+    if (L.routed.num_experts != L0.routed.num_experts || L.routed.hidden != L0.routed.hidden ||
+        L.routed.inter != L0.routed.inter || L.routed.bits != L0.routed.bits ||
+        L.top_k != L0.top_k)
+      return fail(QMOE_ESHAPE, "layer %d differs in shape from layer 0", l);
+    if ((rc = check_vec(norm_w[l], "norm_w[l]"))) return rc;
+  }
+  if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");
+  int rc = check_vec(h0, "h0");
+  if (rc || (rc = check_vec(out, "out"))) return rc;
+  if (h_all && (rc = check_vec(h_all, "h_all"))) return rc;
+  if (h_all && (h_all == out || h_all == h0)) return fail(QMOE_EINVAL, "h_all must not alias h0 or out");
+  if (!topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  const size_t need = qmoe_stack_workspace_bytes(layers, n_layers);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  return hip_status(qmoe::launch_stack(layers, norm_w, n_layers, eps, h0, out, h_all, topk_idx,
+                                       topk_w, ws, (flags & QMOE_STACK_PERSISTENT) != 0,
+                                       static_cast<hipStream_t>(stream)),
+                    "moe_stack_forward launch");
+}
+
 int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* residual,
                               float* out, int32_t T, int32_t* topk_idx, float* topk_w, void* ws,
                               size_t ws_bytes, void* stream) {

@@ -45,6 +45,8 @@
 // workgroup 0 advances the epoch once it has seen every flag.  Every wait is
 // bounded; on time-out a status bit is set and the output is undefined (it never
 // hangs).
+#include <type_traits>
+
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -89,6 +91,47 @@ struct LayerArgs {
   uint64_t* hr;      // [kSlotsH][K][I]
   int E, K;
 };
+
+// A decoder stack in one launch: the workgroups stay resident from layer to layer.
+// Per layer, the weights that differ; the shapes, K and the block offsets are the
+// same for every layer.
+struct StackLayer {
+  const uint8_t* rbase;
+  const uint8_t* sblk;
+  const uint16_t* router;
+  const uint16_t* g;
+  const float* norm_w;
+  int64_t rstride;
+};
+constexpr int kStackMax = 32;  // layers per launch (the table travels as kernel arguments)
+static_assert(kRB == kLine, "a workgroup's output rows fill one line of the stack's hand-over buffer");
+
+struct StackArgs {
+  LayerArgs A;      // layer 0's pointers; x/residual: the stack input, out: its output
+  uint64_t* xbuf;   // [kStackMax][NB][kLine]: layer l's output, one line per workgroup
+  float* h_all;     // [nl][H] every layer's output, or null
+  int nl;
+  StackLayer st[kStackMax];
+};
+
+// the pointers of one layer as the kernel body uses them
+struct LayerPtrs {
+  const uint8_t* rbase;
+  int64_t rstride;
+  const uint8_t* sblk;
+  const uint16_t* router;
+  const uint16_t* g;
+  const float* norm_w;
+  uint64_t *logits, *flags, *hs, *hr;
+  int32_t* idx_out;
+  float* w_out;
+};
+
+__device__ __forceinline__ LayerPtrs ptrs_of(const LayerArgs& A) {
+  return {A.rbase, A.rstride, A.sblk, A.router, A.g, A.norm_w, A.logits, A.flags, A.hs, A.hr,
+          A.idx_out, A.w_out};
+}
+
 
 __device__ __forceinline__ void tag_put(uint64_t* p, float v, uint32_t tag) {
   const uint64_t u = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
@@ -159,8 +202,8 @@ __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) 
   return a0 + a1;
 }
 
-template <int BITS, int H, int I>
-__global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
+template <int BITS, int H, int I, bool STACK, class Args>
+__device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // ---- compile-time geometry
   constexpr int CH = H * BITS / 128;            // 16-byte chunks per gate/up row
   constexpr int LGH = CH >= 64 ? 64 : CH;       // lanes per gate/up row
@@ -186,15 +229,16 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   constexpr int PER_L = (kFusedMaxE + kLB - 1) / kLB;
 
   const int NB = gridDim.x, wg = blockIdx.x;
+  int tx = threadIdx.x;
   // wave-uniform values go through readfirstlane so that their arithmetic (item,
   // expert and row selection, load addresses) runs on the scalar unit
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(tx >> 6));
+  int lane = tx & 63;
   const int rank = wv * NB + wg;
   const int W = NB * kLW;
   const int E = A.E, K = A.K;
-  const int glh = lane % LGH, subh = lane / LGH;
-  const int gli = lane % LGI, subi = lane / LGI;
+  int glh = lane % LGH, subh = lane / LGH;
+  int gli = lane % LGI, subi = lane / LGI;
   const int row0 = wg * kRB;
 
   __shared__ __align__(16) float s_x[H];          // the layer input x
@@ -212,6 +256,22 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __shared__ uint64_t s_cand[kFusedMaxE];      // candidates: key << 32 | ~expert
   __shared__ uint64_t s_pick[kFusedMaxK];      // the picks, in rank order
   bool ok_all = true;
+  LayerPtrs Lp = ptrs_of(A);  // layer 0 (a stack's first layer is described by A too)
+  // a stack's layer table, copied to LDS once: read per layer from the kernel
+  // arguments, the pointers would come through scalar loads that miss, and every
+  // LDS wait after such a load waits for it too
+  __shared__ uint64_t s_tab[STACK ? kStackMax * 6 : 1];
+  uint64_t tab_v = 0;
+  if constexpr (STACK) {
+    static_assert(sizeof(StackLayer) == 6 * sizeof(uint64_t), "six words per layer");
+    tab_v = reinterpret_cast<const uint64_t*>(P.st)[min((int)threadIdx.x, P.nl * 6 - 1)];
+  }
+  // word f of layer l's table entry, as a wave-uniform value
+  auto tab = [&](int l, int f) -> uint64_t {
+    const uint64_t v = s_tab[l * 6 + f];
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  };
 
   // ---- 1. loads: the epoch, x (once per workgroup, into LDS below), the
   //         shared-gate vector and the norm weight, then the router rows.  Every
@@ -221,7 +281,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   //         lets each use below wait for its own data only (a conditional load
   //         makes the compiler wait for everything).
   const uint32_t epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int xi = min((int)threadIdx.x, H / 8 - 1);
+  int xi = min((int)tx, H / 8 - 1);
   float gx[8], nw[8];
   uint4 gq;  // shared-gate vector chunk for gamma (step 8)
   {
@@ -229,8 +289,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     const float4 f1 = reinterpret_cast<const float4*>(A.x + 8 * xi)[1];
     gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
     gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
-    gq = reinterpret_cast<const uint4*>(A.g)[xi];
-    const float* nwp = A.norm_w ? A.norm_w : A.x;  // no norm: a load that is ignored
+    gq = reinterpret_cast<const uint4*>(Lp.g)[xi];
+    const float* nwp = Lp.norm_w ? Lp.norm_w : A.x;  // no norm: a load that is ignored
     const float4 w0 = reinterpret_cast<const float4*>(nwp + 8 * xi)[0];
     const float4 w1 = reinterpret_cast<const float4*>(nwp + 8 * xi)[1];
     nw[0] = w0.x; nw[1] = w0.y; nw[2] = w0.z; nw[3] = w0.w;
@@ -239,22 +299,58 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the rest
   const int quarter = wv & 3;
   uint4 rq[CPLR];
-  auto router_fetch = [&](int row) {  // a row past E reads row E - 1 (not stored)
+  // a row past E reads row E - 1 (not stored)
+  auto router_fetch = [&](const uint16_t* rt, int row, uint4(&dst)[CPLR]) {
     const int rc = min(row, E - 1);
 #pragma unroll
     for (int i = 0; i < CPLR; ++i) {
       const int cq = min(lane + 64 * i, CRQ - 1);
-      rq[i] = ld_stream16(A.router + (int64_t)rc * H + 8 * (quarter * CRQ + cq));
+      dst[i] = ld_stream16(rt + (int64_t)rc * H + 8 * (quarter * CRQ + cq));
     }
   };
-  router_fetch(wg * 2 + (wv >> 2));
+  router_fetch(Lp.router, wg * 2 + (wv >> 2), rq);
 
-  const float resid_v = A.residual[row0 + min((int)threadIdx.x, kRB - 1)];
-  const float resid = (int)threadIdx.x < kRB ? resid_v : 0.f;
-  if (A.norm_w) {
+  const float resid_v = A.residual[row0 + min((int)tx, kRB - 1)];
+  float resid = (int)tx < kRB ? resid_v : 0.f;
+  // the shared expert's loads: one gate/up row pair per rank below I/RPWH and the
+  // wave's shared down item (waves below DITEMS; another wave reads rows it
+  // ignores), into registers
+  const bool has_sp = rank < NSP;
+  int jsp = rank * RPWH + subh;
+  int nl_s = wv * RPWI + subi;
+  RowDot<BITS, LGH, CPLH> dH;
+  auto shared_fetch = [&](const uint8_t* sblk, uint4(&qd)[2][CPLH], uint32_t(&sd)[2][CPLH],
+                          uint4& d0, uint32_t& s0) {
+    const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
+    const uint8_t* cr[2] = {sblk + A.off_g + j * RBH, sblk + A.off_u + j * RBH};
+    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(sblk + A.off_gsb) + j * GH,
+                             reinterpret_cast<const uint32_t*>(sblk + A.off_usb) + j * GH};
+    dH.template fetch_always<2>(cr, sr, glh, qd, sd);
+    // a wave-uniform row base plus a 32-bit lane offset
+    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
+    d0 = ld_stream16(sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
+    s0 = ld_stream4(reinterpret_cast<const uint32_t*>(sblk + A.off_dsb) + (int64_t)rb * GI +
+                    (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
+  };
+  uint4 qsp[2][CPLH];
+  uint32_t ssp[2][CPLH];
+  uint4 dq[1 + MAXR];
+  uint32_t dsc[1 + MAXR];
+  // a stack issues them here for its first layer and, for each later layer, during
+  // the tail of the one before (see the end of step 8)
+  // the next layer's loads (stack only)
+  uint4 gqN, rqN[CPLR];
+  float nwN[8];
+  if constexpr (STACK)
+    if ((int)threadIdx.x < P.nl * 6) s_tab[threadIdx.x] = tab_v;  // seen after the next barrier
+
+  for (int l = 0;;) {
+  if constexpr (STACK)  // per-layer copies: addresses derived from them are not kept live across layers
+    asm volatile("" : "+v"(tx), "+v"(lane), "+v"(glh), "+v"(subh), "+v"(gli), "+v"(subi), "+v"(xi), "+v"(jsp), "+v"(nl_s));
+  if (Lp.norm_w) {
     // RMSNorm of the input stream, computed by every workgroup: x = h / sqrt(mean(h^2) + eps) * w
     float ss = 0.f;
-    if ((int)threadIdx.x < H / 8) {
+    if ((int)tx < H / 8) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(gx[i], gx[i], ss);
     }
@@ -269,16 +365,23 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     for (int i = 0; i < 8; ++i) gx[i] = gx[i] * r * nw[i];
     __syncthreads();  // s_part is reused by the router dots
   }
-  if ((int)threadIdx.x < H / 8) {
-    reinterpret_cast<float4*>(s_x)[2 * threadIdx.x] = make_float4(gx[0], gx[1], gx[2], gx[3]);
-    reinterpret_cast<float4*>(s_x)[2 * threadIdx.x + 1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+  if ((int)tx < H / 8) {
+    reinterpret_cast<float4*>(s_x)[2 * tx] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+    reinterpret_cast<float4*>(s_x)[2 * tx + 1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
   }
   __syncthreads();
 
   // ---- 2. router dots -> logits (every wave has read the epoch itself)
   // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
   uint32_t tag0 = (uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u;
-  tag0 = tag0 ? tag0 : 1u;
+  if constexpr (STACK) {
+    // layer l of a stack is call number epoch + 1 + l (the layers share the
+    // buffers); a run of numbers that would reach 0 restarts at 1
+    const uint32_t nl = (uint32_t)P.nl;
+    tag0 = (tag0 == 0u || tag0 + nl - 1u < tag0) ? 1u + (uint32_t)l : tag0 + (uint32_t)l;
+  } else {
+    tag0 = tag0 ? tag0 : 1u;
+  }
   auto router_rows = [&](int r0) {
     float acc = 0.f;
 #pragma unroll
@@ -294,11 +397,11 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     acc = group_sum_last<64>(acc);
     if (lane == 63) s_part[wv] = acc;
     __syncthreads();
-    if (threadIdx.x < 8) {  // rows r0, r0 + 1 and padding: one whole 64-byte store
-      const bool real = threadIdx.x < 2 && r0 + (int)threadIdx.x < E;
-      const float* pp = s_part + 4 * (threadIdx.x & 1);
+    if (tx < 8) {  // rows r0, r0 + 1 and padding: one whole 64-byte store
+      const bool real = tx < 2 && r0 + (int)tx < E;
+      const float* pp = s_part + 4 * (tx & 1);
       const float v = real ? (pp[0] + pp[1]) + (pp[2] + pp[3]) : 0.f;
-      tag_put(A.logits + (r0 >> 1) * kLine + threadIdx.x, v, tag0);
+      tag_put(Lp.logits + (r0 >> 1) * kLine + tx, v, tag0);
     }
     __syncthreads();
   };
@@ -306,60 +409,40 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // dots wait for those rows only, not for every load issued after them)
   if (wg * 2 < E) router_rows(wg * 2);
   for (int r0 = wg * 2 + NB * 2; r0 < E; r0 += NB * 2) {
-    router_fetch(r0 + (wv >> 2));
+    router_fetch(Lp.router, r0 + (wv >> 2), rq);
     router_rows(r0);
   }
-  // the shared expert's loads go out only now: in step 1 they would share the
-  // start-up burst with the router rows, whose logits everything else waits for
-  const bool has_sp = rank < NSP;
-  const int jsp = rank * RPWH + subh;
-  uint4 qsp[2][CPLH];
-  uint32_t ssp[2][CPLH];
-  RowDot<BITS, LGH, CPLH> dH;
-  {
-    const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
-    const uint8_t* cr[2] = {A.sblk + A.off_g + j * RBH, A.sblk + A.off_u + j * RBH};
-    const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(A.sblk + A.off_gsb) + j * GH,
-                             reinterpret_cast<const uint32_t*>(A.sblk + A.off_usb) + j * GH};
-    dH.template fetch_always<2>(cr, sr, glh, qsp, ssp);
-  }
-  const int nl_s = wv * RPWI + subi;
-  // this wave's shared down item (waves below DITEMS; another wave reads rows it
-  // ignores), into registers: HBM would otherwise idle during the top-K
-  uint4 dq[1 + MAXR];
-  uint32_t dsc[1 + MAXR];
-  {  // a wave-uniform row base plus a 32-bit lane offset
-    const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
-    dq[0] = ld_stream16(A.sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
-    dsc[0] = ld_stream4(reinterpret_cast<const uint32_t*>(A.sblk + A.off_dsb) + (int64_t)rb * GI +
-                        (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
-  }
+  // a single layer issues the shared expert's loads only now: in step 1 they would
+  // share the start-up burst with the router rows, whose logits everything else
+  // waits for (the down item in registers: HBM would otherwise idle during the
+  // top-K)
+  shared_fetch(Lp.sblk, qsp, ssp, dq[0], dsc[0]);
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
-  prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, threadIdx.x, kLB);
-  if (threadIdx.x == 0) {
+  prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
+  if (tx == 0) {
     s_tag = tag0;
     s_ncand = 0;
   }
-  if (threadIdx.x < kFusedMaxK) s_pick[threadIdx.x] = 0;  // no pick: key 0, expert ~0 = -1
+  if (tx < kFusedMaxK) s_pick[tx] = 0;  // no pick: key 0, expert ~0 = -1
   __syncthreads();
   const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_tag);
 
-  uint64_t* hs = A.hs + (size_t)(tag % kSlotsH) * I;
-  uint64_t* hr = A.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
+  uint64_t* hs = Lp.hs + (size_t)(tag % kSlotsH) * I;
+  uint64_t* hr = Lp.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
   // the first poll of logits 0..kLB-1 (step 5) goes out now, unconditionally (a
   // lane past E reads logit E - 1), so that its round trip overlaps the shared
   // gate/up dots; logits from kLB on are first read by the poll loop of step 5
   uint64_t lraw[PER_L];
   uint32_t pending = 0;
   {
-    const int ec = min((int)threadIdx.x, E - 1);
-    lraw[0] = tag_get(A.logits + (ec >> 1) * kLine + (ec & 1));
+    const int ec = min((int)tx, E - 1);
+    lraw[0] = tag_get(Lp.logits + (ec >> 1) * kLine + (ec & 1));
   }
 #pragma unroll
   for (int j = 0; j < PER_L; ++j) {
     if (j) lraw[j] = 0;  // tag 0 is never current: polled in the loop
-    if ((int)threadIdx.x + j * kLB < E) pending |= 1u << j;
+    if ((int)tx + j * kLB < E) pending |= 1u << j;
   }
   dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
   float hs_val = 0.f;
@@ -405,8 +488,8 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 #pragma unroll
       for (int j = 0; j < PER_L; ++j)
         if ((pending >> j) & 1u) {
-          const int e = threadIdx.x + j * kLB;
-          lraw[j] = tag_get(A.logits + (e >> 1) * kLine + (e & 1));
+          const int e = tx + j * kLB;
+          lraw[j] = tag_get(Lp.logits + (e >> 1) * kLine + (e & 1));
         }
     }
     uint32_t lmax = 0;
@@ -427,7 +510,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     for (int j = 0; j < PER_L; ++j)
       if (key[j] != 0 && key[j] >= L) {
         const uint32_t slot = atomicAdd(&s_ncand, 1u);  // key, then the inverted index:
-        s_cand[slot] = ((uint64_t)key[j] << 32) | ~(uint32_t)(threadIdx.x + j * kLB);  // u64 order
+        s_cand[slot] = ((uint64_t)key[j] << 32) | ~(uint32_t)(tx + j * kLB);  // u64 order
       }
     __syncthreads();
   }
@@ -476,12 +559,12 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
 #pragma unroll
     for (int k = 0; k < kFusedMaxK; ++k) wsel[k] *= inv;
   }
-  if (wg == 0 && threadIdx.x == 0) {
+  if (wg == 0 && tx == 0) {
 #pragma unroll
     for (int k = 0; k < kFusedMaxK; ++k)
       if (k < K) {
-        A.idx_out[k] = eidx[k];
-        A.w_out[k] = wsel[k];
+        Lp.idx_out[k] = eidx[k];
+        Lp.w_out[k] = wsel[k];
       }
   }
   if (has_sp && group_last<LGH>(lane)) tag_put(hs + jsp, hs_val, tag);
@@ -507,7 +590,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
       for (int k = 0; k < kFusedMaxK; ++k)
         if (valid && kk[v] == k) e = eidx[k];
       eok[v] = (unsigned)e < (unsigned)E;
-      const uint8_t* blk = A.rbase + (eok[v] ? (int64_t)e * A.rstride : 0);
+      const uint8_t* blk = Lp.rbase + (eok[v] ? (int64_t)e * Lp.rstride : 0);
       cr[2 * v] = blk + A.off_g + jj[v] * RBH;
       cr[2 * v + 1] = blk + A.off_u + jj[v] * RBH;
       sr[2 * v] = reinterpret_cast<const uint32_t*>(blk + A.off_gsb) + jj[v] * GH;
@@ -534,7 +617,7 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     // every output row of the pass lies inside H (H is a multiple of kRB), so a
     // valid expert reads rows row0 + d*RPWI + subi
     const bool ok = (unsigned)e < (unsigned)E;
-    const uint8_t* blk = ok ? A.rbase + (int64_t)e * A.rstride : A.sblk;
+    const uint8_t* blk = ok ? Lp.rbase + (int64_t)e * Lp.rstride : Lp.sblk;
     const int rb = ok ? row0 + d * RPWI : 0;
     dq[1 + m] = ld_stream16(blk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
     dsc[1 + m] = ld_stream4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)rb * GI +
@@ -565,14 +648,14 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   // ~0.5 us here; the flag may instead become visible before some of them, and
   // the reader re-reads any word that still has an old tag.
   __builtin_amdgcn_s_barrier();
-  if (threadIdx.x < 8) tag_put(A.flags + wg * kLine + threadIdx.x, 0.f, tag);
+  if (tx < 8) tag_put(Lp.flags + wg * kLine + tx, 0.f, tag);
   // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
   //         routed down rows (integer dots against the planes of h, codes in
   //         registers since step 6);
   //         combine
-  if ((int)threadIdx.x < NB) {
+  if ((int)tx < NB) {
     uint32_t spins = 0;
-    while ((uint32_t)(tag_get(A.flags + threadIdx.x * kLine) >> 32) != tag) {
+    while ((uint32_t)(tag_get(Lp.flags + tx * kLine) >> 32) != tag) {
       if (++spins > kSpinLimit) {
         ok_all = false;
         break;
@@ -582,17 +665,34 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
   }
   __syncthreads();
   // Every workgroup has read the epoch before tagging its flag: advance it.
-  if (wg == 0 && threadIdx.x == 0)
+  if (wg == 0 && tx == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
       hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag, ok_all);
   __syncthreads();
+  if constexpr (STACK) {
+    // the next layer's loads that do not depend on its input: the shared-gate
+    // vector, the norm weight, the first router rows and the shared expert's rows.
+    // They go out behind the h reads and arrive while the tail below computes.
+    if (l + 1 < P.nl) {
+      const uint16_t* rtN = reinterpret_cast<const uint16_t*>(tab(l + 1, 2));
+      const uint16_t* gN = reinterpret_cast<const uint16_t*>(tab(l + 1, 3));
+      const float* nwN_p = reinterpret_cast<const float*>(tab(l + 1, 4));
+      gqN = reinterpret_cast<const uint4*>(gN)[xi];
+      const float* nwp = nwN_p ? nwN_p : A.x;  // no norm: a load that is ignored
+      const float4 w0 = reinterpret_cast<const float4*>(nwp + 8 * xi)[0];
+      const float4 w1 = reinterpret_cast<const float4*>(nwp + 8 * xi)[1];
+      nwN[0] = w0.x; nwN[1] = w0.y; nwN[2] = w0.z; nwN[3] = w0.w;
+      nwN[4] = w1.x; nwN[5] = w1.y; nwN[6] = w1.z; nwN[7] = w1.w;
+      router_fetch(rtN, wg * 2 + (wv >> 2), rqN);
+    }
+  }
   // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
   // two vectors; unused routed slots hold stale values whose planes are not read)
-  prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, threadIdx.x, kLB);
+  prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, tx, kLB);
   __syncthreads();
   // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
-  const float gpart = group_sum_last<64>((int)threadIdx.x < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
+  const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
   if (lane == 63) s_rv[wv] = gpart;
   // down rows: the wave's shared item (waves below DITEMS) and its MAXR routed
   // items, which all belong to one expert kw, as one branch-free block so that
@@ -638,17 +738,90 @@ __global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < kRB && row0 + (int)threadIdx.x < H) {
+  if ((int)tx < kRB && row0 + (int)tx < H) {
     float gs = 0.f;
 #pragma unroll
     for (int w = 0; w < kLW; ++w) gs += s_rv[w];
     float acc = resid;
 #pragma unroll
     for (int k = 0; k < kFusedMaxK; ++k)
-      if (k < K) acc = fmaf(wsel[k], s_y[k][threadIdx.x], acc);
-    A.out[row0 + threadIdx.x] = fmaf(sigmoid_f(gs), s_y[kFusedMaxK][threadIdx.x], acc);
+      if (k < K) acc = fmaf(wsel[k], s_y[k][tx], acc);
+    const float v = fmaf(sigmoid_f(gs), s_y[kFusedMaxK][tx], acc);
+    if constexpr (STACK) {
+      if (P.h_all) P.h_all[(int64_t)l * H + row0 + tx] = v;
+      if (l + 1 < P.nl) {  // the workgroup's rows fill one line: a single writer
+        tag_put(P.xbuf + ((int64_t)l * NB + wg) * kLine + tx, v, tag);
+        resid = v;
+      } else {
+        A.out[row0 + tx] = v;
+      }
+    } else {
+      A.out[row0 + tx] = v;
+    }
   }
+  if constexpr (!STACK) {
+    break;
+  } else {
+    if (++l == P.nl) break;
+    // ---- 9. (stack) the next layer's input: every workgroup's output line of this
+    //         layer, polled word by word until each carries this call's tag; its
+    //         other loads were issued in step 8
+    {
+      constexpr int XW = H / kLB;  // words per thread
+      uint64_t* xl = P.xbuf + (int64_t)(l - 1) * NB * kLine;
+      uint64_t xv[XW];
+#pragma unroll
+      for (int j = 0; j < XW; ++j) xv[j] = tag_get(xl + tx + j * kLB);
+      uint32_t pend = 0;
+      for (uint32_t spins = 0;; ++spins) {
+#pragma unroll
+        for (int j = 0; j < XW; ++j)
+          if ((uint32_t)(xv[j] >> 32) != tag) pend |= 1u << j;
+          else pend &= ~(1u << j);
+        if (!pend) break;
+        if (spins > kSpinLimit) {
+          ok_all = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < XW; ++j)
+          if ((pend >> j) & 1u) xv[j] = tag_get(xl + tx + j * kLB);
+      }
+#pragma unroll
+      for (int j = 0; j < XW; ++j) s_x[tx + j * kLB] = __uint_as_float((uint32_t)xv[j]);
+      __syncthreads();
+      const float4 f0 = reinterpret_cast<const float4*>(s_x + 8 * xi)[0];
+      const float4 f1 = reinterpret_cast<const float4*>(s_x + 8 * xi)[1];
+      gx[0] = f0.x; gx[1] = f0.y; gx[2] = f0.z; gx[3] = f0.w;
+      gx[4] = f1.x; gx[5] = f1.y; gx[6] = f1.z; gx[7] = f1.w;
+    }
+    Lp.rbase = reinterpret_cast<const uint8_t*>(tab(l, 0));
+    Lp.sblk = reinterpret_cast<const uint8_t*>(tab(l, 1));
+    Lp.router = reinterpret_cast<const uint16_t*>(tab(l, 2));
+    Lp.g = reinterpret_cast<const uint16_t*>(tab(l, 3));
+    Lp.norm_w = reinterpret_cast<const float*>(tab(l, 4));
+    Lp.rstride = (int64_t)tab(l, 5);
+    Lp.idx_out = A.idx_out + l * K;
+    Lp.w_out = A.w_out + l * K;
+    gq = gqN;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) nw[i] = nwN[i];
+#pragma unroll
+    for (int i = 0; i < CPLR; ++i) rq[i] = rqN[i];
+  }
+  }  // layers
   if (!ok_all) flag_status(A.ctrl, 1u);
+}
+
+template <int BITS, int H, int I>
+__global__ __launch_bounds__(kLB, 2) void k_layer(LayerArgs A) {
+  layer_body<BITS, H, I, false>(A, A);
+}
+
+template <int BITS, int H, int I>
+__global__ __launch_bounds__(kLB, 2) void k_stack(StackArgs S) {
+  layer_body<BITS, H, I, true>(S.A, S);
 }
 
 struct FusedCfg {
@@ -690,30 +863,37 @@ UnfusedWs unfused_ws(int E, int K, int H, int I) {
 }
 
 using KernelFn = void (*)(LayerArgs);
+using StackFn = void (*)(StackArgs);
 
-template <int BITS, int H, int I>
-KernelFn pick() {
-  return k_layer<BITS, H, I>;
+template <bool ST>
+using FnOf = typename std::conditional<ST, StackFn, KernelFn>::type;
+
+template <bool ST, int BITS, int H, int I>
+FnOf<ST> pick() {
+  if constexpr (ST)
+    return k_stack<BITS, H, I>;
+  else
+    return k_layer<BITS, H, I>;
 }
 
-template <int BITS, int H>
-KernelFn pick_i(int I) {
-  if (I == 256) return pick<BITS, H, 256>();
-  if (I == 512) return pick<BITS, H, 512>();
-  if (I == 1024) return pick<BITS, H, 1024>();
+template <bool ST, int BITS, int H>
+FnOf<ST> pick_i(int I) {
+  if (I == 256) return pick<ST, BITS, H, 256>();
+  if (I == 512) return pick<ST, BITS, H, 512>();
+  if (I == 1024) return pick<ST, BITS, H, 1024>();
   return nullptr;
 }
 
-template <int BITS>
-KernelFn pick_h(int H, int I) {
-  if (H == 1024) return pick_i<BITS, 1024>(I);
-  if (H == 2048) return pick_i<BITS, 2048>(I);
-  if (H == 4096) return pick_i<BITS, 4096>(I);
+template <bool ST, int BITS>
+FnOf<ST> pick_h(int H, int I) {
+  if (H == 1024) return pick_i<ST, BITS, 1024>(I);
+  if (H == 2048) return pick_i<ST, BITS, 2048>(I);
+  if (H == 4096) return pick_i<ST, BITS, 4096>(I);
   return nullptr;
 }
 
 // grid geometry for the fused kernel, or nb == 0 when the shape needs the fallback
-FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
+FusedCfg fused_config(const qmoe_layer& L, const void* fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
@@ -721,8 +901,7 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   const int cus = device_cus();
   if (cus <= 0) return c;
   int blocks_per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, reinterpret_cast<const void*>(fn),
-                                                   kLB, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, fn, kLB, 0) != hipSuccess ||
       blocks_per_cu < 1)
     return c;
   const int nb = H / kRB;
@@ -739,9 +918,59 @@ FusedCfg fused_config(const qmoe_layer& L, KernelFn fn) {
   return c;
 }
 
-KernelFn fused_kernel(const qmoe_layer& L) {
+template <bool ST>
+FnOf<ST> fused_kernel(const qmoe_layer& L) {
   const int H = L.routed.hidden, I = L.routed.inter;
-  return L.routed.bits == 4 ? pick_h<4>(H, I) : pick_h<2>(H, I);
+  return L.routed.bits == 4 ? pick_h<ST, 4>(H, I) : pick_h<ST, 2>(H, I);
+}
+
+LayerArgs layer_args(const qmoe_layer& L, const float* x, const float* norm_w, float eps,
+                     const float* residual, float* out, int32_t* idx, float* w, uint8_t* wsb) {
+  const int E = L.routed.num_experts, H = L.routed.hidden, I = L.routed.inter;
+  const WsLayout wl = fused_ws(E, H, I);
+  const qmoe_expert_offsets o = expert_offsets(H, I, L.routed.bits);
+  LayerArgs A;
+  A.rbase = static_cast<const uint8_t*>(L.routed.base);
+  A.rstride = L.routed.stride;
+  A.sblk = static_cast<const uint8_t*>(L.shared.base);
+  A.off_g = o.gate_codes;
+  A.off_u = o.up_codes;
+  A.off_d = o.down_codes;
+  A.off_gsb = o.gate_sb;
+  A.off_usb = o.up_sb;
+  A.off_dsb = o.down_sb;
+  A.router = L.router;
+  A.g = L.shared_gate;
+  A.x = x;
+  A.norm_w = norm_w;
+  A.eps = eps;
+  A.residual = residual;
+  A.out = out;
+  A.idx_out = idx;
+  A.w_out = w;
+  A.ctrl = reinterpret_cast<uint32_t*>(wsb + wl.ctrl);
+  A.logits = reinterpret_cast<uint64_t*>(wsb + wl.logits);
+  A.flags = reinterpret_cast<uint64_t*>(wsb + wl.flags);
+  A.hs = reinterpret_cast<uint64_t*>(wsb + wl.hs);
+  A.hr = reinterpret_cast<uint64_t*>(wsb + wl.hr);
+  A.E = E;
+  A.K = L.top_k;
+  return A;
+}
+
+// stack workspace: the single layer's (every layer of a launch uses its buffers,
+// each with its own call number), then the output lines of each layer
+struct StackWs {
+  int64_t xbuf, total;
+};
+
+StackWs stack_ws(const qmoe_layer& L, int n) {
+  const WsLayout wl = fused_ws(L.routed.num_experts, L.routed.hidden, L.routed.inter);
+  const int nl = n < kStackMax ? n : kStackMax;
+  StackWs w;
+  w.xbuf = wl.total;
+  w.total = w.xbuf + align256((int64_t)nl * (L.routed.hidden / kRB) * kLine * 8);
+  return w;
 }
 
 }  // namespace
@@ -758,37 +987,10 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w
                         hipStream_t s) {
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
-  KernelFn fn = fused_kernel(L);
-  const FusedCfg cfg = fused_config(L, fn);
+  KernelFn fn = fused_kernel<false>(L);
+  const FusedCfg cfg = fused_config(L, reinterpret_cast<const void*>(fn));
   if (cfg.nb > 0) {
-    const WsLayout wl = fused_ws(E, H, I);
-    const qmoe_expert_offsets o = expert_offsets(H, I, L.routed.bits);
-    LayerArgs A;
-    A.rbase = static_cast<const uint8_t*>(L.routed.base);
-    A.rstride = L.routed.stride;
-    A.sblk = static_cast<const uint8_t*>(L.shared.base);
-    A.off_g = o.gate_codes;
-    A.off_u = o.up_codes;
-    A.off_d = o.down_codes;
-    A.off_gsb = o.gate_sb;
-    A.off_usb = o.up_sb;
-    A.off_dsb = o.down_sb;
-    A.router = L.router;
-    A.g = L.shared_gate;
-    A.x = x;
-    A.norm_w = norm_w;
-    A.eps = eps;
-    A.residual = residual;
-    A.out = out;
-    A.idx_out = idx;
-    A.w_out = w;
-    A.ctrl = reinterpret_cast<uint32_t*>(wsb + wl.ctrl);
-    A.logits = reinterpret_cast<uint64_t*>(wsb + wl.logits);
-    A.flags = reinterpret_cast<uint64_t*>(wsb + wl.flags);
-    A.hs = reinterpret_cast<uint64_t*>(wsb + wl.hs);
-    A.hr = reinterpret_cast<uint64_t*>(wsb + wl.hr);
-    A.E = E;
-    A.K = K;
+    const LayerArgs A = layer_args(L, x, norm_w, eps, residual, out, idx, w, wsb);
     hipLaunchKernelGGL(fn, dim3(cfg.nb), dim3(kLB), 0, s, A);
     return hipGetLastError();
   }
@@ -810,6 +1012,59 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w
   if (err == hipSuccess) err = launch_ffn(L.shared, zero_idx, 1, x, 0, ys, h, s);
   if (err == hipSuccess) err = launch_combine(yr, w, ys, L.shared_gate, x, residual, out, H, K, s);
   return err;
+}
+
+size_t stack_workspace_bytes(const qmoe_layer& L, int n_layers) {
+  const size_t st = (size_t)stack_ws(L, n_layers).total;
+  const size_t one = layer_workspace_bytes(L);
+  return st > one ? st : one;
+}
+
+hipError_t launch_stack(const qmoe_layer* Ls, const float* const* norm_w, int n, float eps,
+                        const float* h0, float* out, float* h_all, int32_t* idx, float* w, void* ws,
+                        bool persistent, hipStream_t s) {
+  const qmoe_layer& L0 = Ls[0];
+  const int K = L0.top_k, H = L0.routed.hidden;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  StackFn fn = persistent ? fused_kernel<true>(L0) : nullptr;
+  const FusedCfg cfg = fn ? fused_config(L0, reinterpret_cast<const void*>(fn)) : FusedCfg{};
+  hipError_t err = hipSuccess;
+  if (cfg.nb == 0) {  // one launch per layer: layer l reads layer l-1's output
+    const float* cur = h0;
+    for (int l = 0; l < n && err == hipSuccess; ++l) {
+      float* dst = h_all ? h_all + (int64_t)l * H : out;
+      err = launch_layer(Ls[l], cur, norm_w[l], eps, cur, dst, idx + l * K, w + l * K, ws, s);
+      cur = dst;
+    }
+    if (err == hipSuccess && h_all)
+      err = hipMemcpyAsync(out, cur, (size_t)H * 4, hipMemcpyDeviceToDevice, s);
+    return err;
+  }
+  const StackWs sw = stack_ws(L0, n);
+  // launches of up to kStackMax layers; a later launch reads its input from out
+  // (every workgroup reads its input before any writes its rows of out)
+  for (int c0 = 0; c0 < n; c0 += kStackMax) {
+    const int nl = n - c0 < kStackMax ? n - c0 : kStackMax;
+    const float* xin = c0 == 0 ? h0 : out;
+    StackArgs S;
+    S.A = layer_args(Ls[c0], xin, norm_w[c0], eps, xin, out, idx + (int64_t)c0 * K,
+                     w + (int64_t)c0 * K, wsb);
+    S.xbuf = reinterpret_cast<uint64_t*>(wsb + sw.xbuf);
+    S.h_all = h_all ? h_all + (int64_t)c0 * H : nullptr;
+    S.nl = nl;
+    for (int i = 0; i < nl; ++i) {
+      const qmoe_layer& Li = Ls[c0 + i];
+      S.st[i].rbase = static_cast<const uint8_t*>(Li.routed.base);
+      S.st[i].sblk = static_cast<const uint8_t*>(Li.shared.base);
+      S.st[i].router = Li.router;
+      S.st[i].g = Li.shared_gate;
+      S.st[i].norm_w = norm_w[c0 + i];
+      S.st[i].rstride = Li.routed.stride;
+    }
+    hipLaunchKernelGGL(fn, dim3(cfg.nb), dim3(kLB), 0, s, S);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qmoe

@@ -44,6 +44,13 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w
                         const float* residual, float* out, int32_t* idx, float* w, void* ws,
                         hipStream_t s);
 
+// a decoder stack of n layers of one shape, h <- h + MoE_l(rmsnorm(h, norm_w[l])):
+// one fused launch per layer, or (persistent) one launch per 32 layers (layer.hip)
+size_t stack_workspace_bytes(const qmoe_layer& L, int n_layers);
+hipError_t launch_stack(const qmoe_layer* layers, const float* const* norm_w, int n, float eps,
+                        const float* h0, float* out, float* h_all, int32_t* idx, float* w, void* ws,
+                        bool persistent, hipStream_t s);
+
 // batched decode (batched.hip)
 size_t batched_workspace_bytes(const qmoe_layer& L, int T);
 hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float* residual,

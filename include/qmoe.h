@@ -177,6 +177,39 @@ int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* nor
                            void* stream);
 
 /*
+ * A decoder stack for one token: for l = 0 .. n_layers-1,
+ * h <- h + MoE_l(rmsnorm(h, norm_w[l])), each layer as in moe_layer_forward_norm
+ * ([PK] "지연 GPU 전문가 실행 (Deferred CMD3)": the combined, normalised output
+ * of one layer is the next layer's input with no host round trip).
+ *   layers: host array [n_layers]; every layer has the same E, H, I, bits and K;
+ *   norm_w: host array [n_layers] of device float [H] (16-byte aligned);
+ *   h0: device float [H], the input; out: device float [H], the output (may alias h0);
+ *   h_all: device float [n_layers][H], each layer's output, or NULL (must not alias
+ *   h0 or out);
+ *   topk_idx/topk_w: device [n_layers][K] (written);
+ *   flags: 0, or QMOE_STACK_PERSISTENT: up to 32 layers per launch, the workgroups
+ *   staying resident from layer to layer (each layer's output reaches the next
+ *   through the workspace; the next layer's router rows, gate vector and norm
+ *   weight load during the current layer's tail).  Both give the same result bit
+ *   for bit.  Without the flag each layer is one fused launch, which measures
+ *   faster on MI355X: the device-side hand-off costs as much as a kernel boundary,
+ *   and the layer loop compiles to a slower kernel;
+ *   ws: at least qmoe_stack_workspace_bytes(layers, n_layers) bytes, 256-byte
+ *   aligned, zero-filled before its first use; it may serve moe_layer_forward
+ *   calls too, but no two calls may use it at the same time.
+ * Errors: as moe_layer_forward_norm; QMOE_ESHAPE if a layer's shape differs from
+ * layer 0's; QMOE_EINVAL for unknown flags.  Word 1 of the workspace is the status
+ * word of moe_layer_forward.
+ */
+#define QMOE_STACK_PERSISTENT 1
+int moe_stack_forward(const qmoe_layer* layers, const float* const* norm_w, int32_t n_layers,
+                      float eps, const float* h0, float* out, float* h_all, int32_t* topk_idx,
+                      float* topk_w, int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_stack_forward (0 if layers is NULL or n_layers < 1). */
+size_t qmoe_stack_workspace_bytes(const qmoe_layer* layers, int32_t n_layers);
+
+/*
  * Batched decode of T tokens through one layer (row t equals moe_layer_forward on
  * token t): tokens are grouped per routed expert (histogram, scan, stable scatter)
  * so each active expert's weights are read once per batch.

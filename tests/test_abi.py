@@ -92,6 +92,26 @@ def test_invalid_arguments_are_rejected_before_launch():
         q.QMOE_EALIGN
     assert lib.rmsnorm_f32(16, 16, -1.0, 4, 16, None) == q.QMOE_EINVAL
     assert lib.qmoe_workspace_bytes(ctypes.byref(L), 0) == 0
+    # stack: no layers, shapes that differ between layers, a short workspace
+    Ls = (q.LayerC * 2)(L, L)
+    nw = (ctypes.c_void_p * 2)(256, 256)
+    need_s = lib.qmoe_stack_workspace_bytes(Ls, 2)
+    assert need_s >= need and lib.qmoe_stack_workspace_bytes(Ls, 0) == 0
+    assert lib.qmoe_stack_workspace_bytes(None, 2) == 0
+    assert lib.moe_stack_forward(Ls, nw, 0, 1e-6, 256, 512, None, 16, 16, 0, 256, need_s, None) == q.QMOE_EINVAL
+    assert lib.moe_stack_forward(None, nw, 2, 1e-6, 256, 512, None, 16, 16, 0, 256, need_s, None) == q.QMOE_EINVAL
+    assert lib.moe_stack_forward(Ls, nw, 2, 1e-6, 256, 512, None, 16, 16, 0, 256, need_s - 1, None) == \
+        q.QMOE_EWORKSPACE
+    assert lib.moe_stack_forward(Ls, nw, 2, 1e-6, 256, 512, 520, 16, 16, 0, 256, need_s, None) == q.QMOE_EALIGN
+    assert lib.moe_stack_forward(Ls, nw, 2, 1e-6, 256, 512, None, 16, 16, 2, 256, need_s, None) == q.QMOE_EINVAL
+    assert lib.moe_stack_forward(Ls, nw, 2, 1e-6, 256, 512, 512, 16, 16, 0, 256, need_s, None) == q.QMOE_EINVAL
+    L2b = q.LayerC(q.ExpertPoolC(256, 3932160, 512, 4096, 1024, 2), q.ExpertPoolC(256, 3932160, 1, 4096, 1024, 2),
+                   256, 256, 4)
+    Lmix = (q.LayerC * 2)(L, L2b)
+    assert lib.moe_stack_forward(Lmix, nw, 2, 1e-6, 256, 512, None, 16, 16, 0, 256, need_s, None) == q.QMOE_ESHAPE
+    # more layers than one launch holds: the buffers of one launch's worth
+    assert lib.qmoe_stack_workspace_bytes((q.LayerC * 40)(*([L] * 40)), 40) == \
+        lib.qmoe_stack_workspace_bytes((q.LayerC * 32)(*([L] * 32)), 32)
     assert lib.qmoe_strerror(q.QMOE_EWORKSPACE) == b"workspace too small"
 
 

@@ -406,8 +406,69 @@ def test_batched_parity(q, E, H, I, bits, K, T):
 # layer stack (RMSNorm before every layer, residual = pre-norm h)
 # ---------------------------------------------------------------------------
 
+def _chain(q, layers, dnorm, h0, ws):
+    """One moe_layer_forward_norm launch per layer, in place: each layer's output, idx, w."""
+    h = h0.clone()
+    outs, idxs, wts = [], [], []
+    for l, D in enumerate(layers):
+        _, idx, w = q.moe_layer_forward_norm(D.L, h, dnorm[l], 1e-6, out=h, ws=ws)
+        outs.append(h.clone())
+        idxs.append(idx.clone())
+        wts.append(w.clone())
+    return torch.stack(outs), torch.stack(idxs), torch.stack(wts)
+
+
+def _stack_case(q, seed, E, H, I, bits, K, nl, tokens, oracle_layers):
+    layers = [DeviceLayer(seed, l, E, H, I, bits, K) for l in range(nl)]
+    norm_w = [synth.norm_weight(seed, l, H) for l in range(nl)]
+    dnorm = [torch.from_numpy(w).cuda() for w in norm_w]
+    S = q.Stack([D.L for D in layers], dnorm)
+    ws = q.alloc_stack_workspace(S)
+    ws_chain = q.alloc_workspace(layers[0].L)
+    for tok in tokens:  # later calls run with the next call number on the same workspace
+        h0 = host_x(seed, tok, H)
+        hd = torch.from_numpy(h0).cuda()
+        co, ci, cw = _chain(q, layers, dnorm, hd, ws_chain)
+        for persistent in (False, True):
+            h_all = torch.full((nl, H), float("nan"), dtype=torch.float32, device="cuda")
+            out, idx, w = q.moe_stack_forward(S, hd, 1e-6, h_all=h_all, ws=ws, persistent=persistent)
+            out2, idx2, _ = q.moe_stack_forward(S, hd, 1e-6, ws=ws, persistent=persistent)  # no h_all
+            torch.cuda.synchronize()
+            assert _status(ws) == 0 and _status(ws_chain) == 0
+            # the same arithmetic as one launch per layer: equal bit for bit
+            same = [bool(torch.equal(co[l], h_all[l])) for l in range(nl)]
+            say("  token", tok, "persistent" if persistent else "per layer",
+                "layers equal to the single-layer launches:", sum(same), "of", nl)
+            assert torch.equal(ci, idx) and torch.equal(cw, w) and torch.equal(idx2, idx)
+            assert all(same) and torch.equal(out, h_all[-1]) and torch.equal(out2, out)
+        # the oracle, fed the GPU's input to each checked layer
+        HA, IDX, W = h_all.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+        for l in oracle_layers:
+            hprev = (h0 if l == 0 else HA[l - 1]).astype(np.float64)
+            xr = oracle.rmsnorm(hprev, norm_w[l], 1e-6)
+            _check_layer_token(layers[l], xr, HA[l], IDX[l], W[l], residual=hprev)
+
+
+STACK_CASES = [  # (E, H, I, bits, K, layers) -- fused shapes, then one the fallback chain serves
+    (64, 1024, 256, 4, 4, 5), (64, 1024, 256, 2, 4, 3), (100, 2048, 512, 4, 3, 3), (16, 192, 128, 4, 2, 3),
+]
+
+
+@pytest.mark.parametrize("E,H,I,bits,K,nl", STACK_CASES)
+def test_stack_kernel_matches_layer_launches_and_oracle(q, E, H, I, bits, K, nl):
+    say("stack kernel", E, H, I, bits, K, nl)
+    _stack_case(q, 1003, E, H, I, bits, K, nl, tokens=(0, 1), oracle_layers=range(nl))
+
+
+def test_stack_kernel_more_layers_than_one_launch(q):
+    """34 layers: two launches (32 + 2); the oracle checks the layers around the seam."""
+    say("stack kernel, 34 layers")
+    _stack_case(q, 1003, 64, 1024, 256, 4, 4, 34, tokens=(0,), oracle_layers=(0, 30, 31, 32, 33))
+
+
 def test_stack_parity(q):
-    """A 3-layer stack at the workload's per-layer shape, 2 tokens, end to end."""
+    """A 3-layer stack at the workload's per-layer shape, 2 tokens, end to end: one
+    launch per layer against the oracle, and the stack kernel against both."""
     L_, E, H, I, K = 3, 512, 4096, 1024, 4
     seed = 1003
     say("stack", L_, "layers")
@@ -415,15 +476,20 @@ def test_stack_parity(q):
     norm_w = [synth.norm_weight(seed, l, H) for l in range(L_)]
     dnorm = [torch.from_numpy(w).cuda() for w in norm_w]
     ws = [q.alloc_workspace(D.L) for D in layers]
+    S = q.Stack([D.L for D in layers], dnorm)
+    ws_s = q.alloc_stack_workspace(S)
     for tok in range(2):
         h0 = host_x(seed, tok, H)
         h = torch.from_numpy(h0).cuda()
+        out_s, idx_s, _ = q.moe_stack_forward(S, h.clone(), 1e-6, ws=ws_s, persistent=True)
         gpu_idx = []
         for l, D in enumerate(layers):
             # one launch per layer, in place: h <- h + MoE(rmsnorm(h))
             _, idx, _ = q.moe_layer_forward_norm(D.L, h, dnorm[l], 1e-6, out=h, ws=ws[l])
             gpu_idx.append(idx.cpu().numpy())
         torch.cuda.synchronize()
+        assert _status(ws_s) == 0
+        assert torch.equal(out_s, h) and (idx_s.cpu().numpy() == np.stack(gpu_idx)).all()
         # oracle end to end; a near-tie is resolved the way the GPU did after checking validity
         hr = h0.astype(np.float64)
         for l, D in enumerate(layers):
