@@ -35,6 +35,9 @@ Readings of the pages where they are silent (each listed in the design notes):
 * Combine: ``out = residual + sum_i w_i * y_i + sigmoid(g . x) * y_shared``;
   the sigmoid gate scales the shared expert only.
 * RMSNorm: ``v / sqrt(mean(v^2) + eps) * w``.
+* GatedDeltaNet: the pages name a scale, a matrix-vector product and a rank-1
+  update of a 128x128 state per head; read as the delta rule with a decay gate
+  (``gdn_step``), with q, k, v and the two gates given.
 
 Parity status of each function is stated in its docstring; every function here
 is pinned by a test in ``tests/test_oracle_pins.py`` against hand-built cases,
@@ -361,6 +364,44 @@ def moe_stack(layers, h0: np.ndarray, hidden, inter, bits, top_k, eps=1e-6):
         h = moe_layer(L["get_expert"], L["shared_block"], L["router"], L["shared_gate"],
                       x, h, hidden, inter, bits, top_k)
     return h
+
+
+# --------------------------------------------------------------------------
+# GatedDeltaNet recurrence   ([PK] "Accelerate BLAS 활용" / [GN] "핵심 기술":
+# the linear-attention layers update a 128x128 state per head, 64 heads, with a
+# scale, a matrix-vector product and a rank-1 update; [PK] architecture: 45 of
+# the 60 layers are GatedDeltaNet layers)
+# --------------------------------------------------------------------------
+
+def gdn_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, alpha: np.ndarray,
+             beta: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """One token of the gated delta rule for every head.
+
+    S: [heads][dk][dv], the state: S[h]^T k is the value the head recalls for the
+    key k.  q, k: [heads][dk]; v: [heads][dv]; alpha (decay) and beta (write
+    strength): [heads].  Per head, in the order of the pages' three BLAS calls:
+      S <- alpha S                      (scale)
+      u  = S^T k                        (matrix-vector: what the key recalls now)
+      S <- S + k (beta (v - u))^T       (rank-1 update: move that recall toward v)
+      o  = S^T q                        (the read-out of the updated state)
+    The pages name the operations only; this is the delta rule with a decay gate,
+    taking q, k, v, alpha and beta as given (their projections, normalisation and
+    the gates' nonlinearities come before the recurrence).  Returns (S', o).
+    """
+    S = np.array(S, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64).reshape(-1)
+    beta = np.asarray(beta, dtype=np.float64).reshape(-1)
+    heads = S.shape[0]
+    o = np.zeros((heads, S.shape[2]))
+    for h in range(heads):
+        S[h] = alpha[h] * S[h]
+        u = S[h].T @ k[h]
+        S[h] = S[h] + np.outer(k[h], beta[h] * (v[h] - u))
+        o[h] = S[h].T @ q[h]
+    return S, o
 
 
 # --------------------------------------------------------------------------

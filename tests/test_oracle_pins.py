@@ -416,3 +416,95 @@ def test_stack_feeds_normalised_input():
     S = 3.0 / math.sqrt(9.0 + 1e-6)        # sum of x
     y = I * 0.5 * 2.0 * S * oracle.silu(S)  # constant-expert output for sum(x) = S
     np.testing.assert_allclose(out, h0 + y + 0.5 * y, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# GatedDeltaNet recurrence
+# --------------------------------------------------------------------------
+
+def _gdn_inputs(rng, heads, dk, dv):
+    S = rng.standard_normal((heads, dk, dv))
+    q = rng.standard_normal((heads, dk))
+    k = rng.standard_normal((heads, dk))
+    v = rng.standard_normal((heads, dv))
+    return S, q, k, v
+
+
+def test_gdn_delta_rule_stores_the_value_at_its_key():
+    """beta = 1 and a unit key: afterwards the key recalls exactly v, whatever the
+    decay and the (non-symmetric) state held before -- the defining property of
+    the delta rule.  A transposed state, a decay missing from the recall or a
+    wrong sign all break it."""
+    rng = np.random.default_rng(11)
+    S, q, k, v = _gdn_inputs(rng, 3, 5, 4)
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    alpha = np.array([1.0, 0.5, 0.9])
+    S2, _ = oracle.gdn_step(S, q, k, v, alpha, np.ones(3))
+    for h in range(3):
+        recall = np.array([sum(S2[h, i, j] * k[h, i] for i in range(5)) for j in range(4)])
+        np.testing.assert_allclose(recall, v[h], rtol=0, atol=1e-12)
+
+
+def test_gdn_zero_state_closed_form():
+    """From a zero state: S' = beta k v^T and o = beta (k . q) v."""
+    rng = np.random.default_rng(12)
+    _, q, k, v = _gdn_inputs(rng, 2, 4, 3)
+    beta = np.array([0.25, 0.75])
+    S2, o = oracle.gdn_step(np.zeros((2, 4, 3)), q, k, v, np.array([0.3, 0.6]), beta)
+    for h in range(2):
+        for i in range(4):
+            for j in range(3):
+                assert S2[h, i, j] == pytest.approx(beta[h] * k[h, i] * v[h, j], rel=1e-14)
+        kq = sum(k[h, i] * q[h, i] for i in range(4))
+        np.testing.assert_allclose(o[h], beta[h] * kq * v[h], rtol=1e-13)
+
+
+def test_gdn_gates_off_and_decay_only():
+    """beta = 0: the state only decays (alpha = 1: it is unchanged) and the
+    output is the decayed state read at q, summed by hand."""
+    rng = np.random.default_rng(13)
+    S, q, k, v = _gdn_inputs(rng, 2, 3, 4)
+    for alpha in (1.0, 0.25):
+        S2, o = oracle.gdn_step(S, q, k, v, np.full(2, alpha), np.zeros(2))
+        np.testing.assert_array_equal(S2, alpha * S)
+        for h in range(2):
+            for j in range(4):
+                assert o[h, j] == pytest.approx(alpha * sum(S[h, i, j] * q[h, i] for i in range(3)), rel=1e-13)
+
+
+def test_gdn_orthogonal_keys_do_not_interfere():
+    """A state holding values at orthonormal keys (S = sum_m k_m v_m^T): writing a
+    new value at key 0 leaves what the other keys recall untouched, and the output
+    for q = key m is the value stored there."""
+    rng = np.random.default_rng(14)
+    dk, dv = 6, 5
+    Q, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Q.T                                   # rows: orthonormal keys
+    vals = rng.standard_normal((dk, dv))
+    S = sum(np.outer(keys[m], vals[m]) for m in range(dk))[None]
+    vnew = rng.standard_normal((1, dv))
+    for m in range(1, dk):
+        S2, o = oracle.gdn_step(S, keys[m][None], keys[0][None], vnew, np.ones(1), np.ones(1))
+        np.testing.assert_allclose(o[0], vals[m], atol=1e-12)
+    np.testing.assert_allclose(S2[0].T @ keys[0], vnew[0], atol=1e-12)
+
+
+def test_gdn_steps_compose():
+    """Two tokens through the recurrence equal the explicit two-step formula
+    S2 = a2 (a1 S + k1 d1^T) + k2 d2^T with d_t = b_t (v_t - recall), written out
+    element by element on a tiny case."""
+    rng = np.random.default_rng(15)
+    dk, dv = 3, 2
+    S = rng.standard_normal((1, dk, dv))
+    qs, ks, vs = rng.standard_normal((2, dk)), rng.standard_normal((2, dk)), rng.standard_normal((2, dv))
+    a, b = [0.7, 0.9], [0.4, 0.8]
+    St = S.copy()
+    for t in range(2):
+        St, _ = oracle.gdn_step(St, qs[t][None], ks[t][None], vs[t][None], np.array([a[t]]), np.array([b[t]]))
+    M = [[S[0, i, j] for j in range(dv)] for i in range(dk)]
+    for t in range(2):
+        M = [[a[t] * M[i][j] for j in range(dv)] for i in range(dk)]
+        rec = [sum(M[i][j] * ks[t][i] for i in range(dk)) for j in range(dv)]
+        d = [b[t] * (vs[t][j] - rec[j]) for j in range(dv)]
+        M = [[M[i][j] + ks[t][i] * d[j] for j in range(dv)] for i in range(dk)]
+    np.testing.assert_allclose(St[0], np.array(M), rtol=1e-13)
