@@ -12,6 +12,9 @@ Workloads (all weights 4-bit unless noted; H = 4096, I = 1024, group 64):
                         layer; a step is one token through all 60 layers
   --config 4            batched decode of 64 tokens through the config-1 layer;
                         a step is one batch
+  --config 5            one GatedDeltaNet recurrence step (64 heads x 128x128
+                        fp32 state) on a ring of 128 resident states; a step is
+                        one call
 Inputs are synthetic (seeded Philox streams generated in HBM); weights and
 activations are resident in HBM before the timed region starts.  Steps are
 enqueued as replays of HIP graphs, so the host never synchronises inside the
@@ -325,6 +328,60 @@ def run_ffn_bench(args, torch, q, synth):
             "cfg": {"experts_resident": n_exp}}
 
 
+def run_gdn_bench(args, torch, q, synth):
+    """One GatedDeltaNet decode step per step (64 heads x 128x128 fp32 state), on a
+    state taken in turn from a ring of 128 (512 MB, more than the last-level cache)."""
+    import numpy as np
+    heads, dk, dv, ring, n_tok = 64, 128, 128, 128, 64
+    seed = 1005
+    states = torch.empty(ring, heads, dv, dk, dtype=torch.float32, device="cuda")
+    synth.fill_normal_f32(states, seed, synth.tensor_id(synth.K_GDN_STATE, 0, 0), synth.GDN_STATE_SIGMA)
+    toks = [synth.gdn_token(seed, 0, t, heads, dk, dv) for t in range(n_tok)]
+    Qs, Ks, Vs, As, Bs = (torch.from_numpy(np.stack([t[i] for t in toks])).cuda() for i in range(5))
+    o = torch.empty(heads, dv, dtype=torch.float32, device="cuda")
+    calls = [(lambda i=i: q.gdn_recurrent_step(states[i % ring], Qs[i % n_tok], Ks[i % n_tok], Vs[i % n_tok],
+                                               As[i % n_tok], Bs[i % n_tok], o=o)) for i in range(ring)]
+    steps = max(1, args.steps)
+    dt = timed_steps(torch, calls, steps, args.warmup, ring)
+    if not bool(torch.isfinite(states).all()):
+        raise RuntimeError("GatedDeltaNet state went non-finite")
+    # the same bytes moved by a plain device copy (4 MB read + 4 MB written), timed alike
+    copies = [(lambda i=i: states[(i + 1) % ring].copy_(states[i])) for i in range(ring)]
+    copy_s = timed_steps(torch, copies, 1024, 128, ring) / 1024
+    per_step = 2 * heads * dv * dk * 4 + (2 * heads * dk + 2 * heads * dv + 2 * heads) * 4
+    launch_s = dt / steps
+    roof = {"bound": "hbm", "achieved": round(per_step / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(per_step / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles("k_gdn")}
+    extra = {"kernel": "gdn_recurrent_step (k_gdn<128>)", "bytes_per_step": per_step,
+             "avg_step_us": round(launch_s * 1e6, 3), "copy_4MB_us": round(copy_s * 1e6, 3),
+             "copy_4MB_GBps": round(2 * heads * dk * dv * 4 / copy_s / 1e9, 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_gdn(seed, heads, dk, dv, args.cpu_seconds)
+    return {"value": steps / dt, "unit": "recurrence steps/s", "steps": steps, "dt": dt, "roof": roof,
+            "extra": extra, "cpu": cpu, "workload": "gdn_decode_step_64x128x128", "bits": None,
+            "metric": "GatedDeltaNet decode steps/s (64 heads x 128x128 fp32 state), batch 1",
+            "config": {"workload": "gdn_decode_step_64x128x128", "heads": heads, "dk": dk, "dv": dv,
+                       "state_ring": ring, "state_ring_MB": ring * heads * dk * dv * 4 >> 20}}
+
+
+def cpu_oracle_gdn(seed, heads, dk, dv, target_s):
+    """The oracle's recurrence step (float64, numpy) on the host, repeated for about
+    target_s seconds on one state."""
+    import oracle
+    import synth
+    S = synth.gdn_state(seed, 0, heads, dk, dv).transpose(0, 2, 1).astype("float64")
+    toks = [synth.gdn_token(seed, 0, t, heads, dk, dv) for t in range(8)]
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        S, _ = oracle.gdn_step(S, *toks[n % 8])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "recurrence steps/s", "cores": blas_threads(),
+            "kind": "oracle", "sample": f"{n} steps of 64 heads x 128x128 on one state"}
+
+
 def cpu_oracle_ffn(seed, n_exp, target_s):
     import oracle
     import synth
@@ -461,7 +518,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16384)
     ap.add_argument("--warmup", type=int, default=1024)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--persistent", action="store_true",
@@ -497,15 +554,17 @@ def main():
         r = run_ffn_bench(args, torch, q, synth)
     elif args.config == 3:
         r = run_stack_bench(args, torch, q, synth)
+    elif args.config == 5:
+        r = run_gdn_bench(args, torch, q, synth)
     else:
         r = run_batched_bench(args, torch, q, synth)
     r["extra"].update(extra0)
-    config = {"workload": r["workload"], "experts": E, "hidden": H, "inter": I, "top_k": K,
-              "shared_experts": 1, "group": 64, "bits": r["bits"]}
-    config.update(r["cfg"])
+    config = r.get("config") or {"workload": r["workload"], "experts": E, "hidden": H, "inter": I,
+                                 "top_k": K, "shared_experts": 1, "group": 64, "bits": r["bits"]}
+    config.update(r.get("cfg", {}))
     config["device"] = torch.cuda.get_device_name(0)
     line = {
-        "metric": METRIC, "value": round(r["value"], 1), "unit": r["unit"], "n_gpus": 1,
+        "metric": r.get("metric", METRIC), "value": round(r["value"], 1), "unit": r["unit"], "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["dt"] * 1e3 / r["steps"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": config,

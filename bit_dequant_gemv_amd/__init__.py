@@ -76,6 +76,7 @@ _SIGS = {
                            _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
     "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
     "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
+    "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp], ctypes.c_int),
     "qmoe_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "qmoe_last_error": ([], ctypes.c_char_p),
 }
@@ -340,6 +341,22 @@ def moe_layer_forward_batched(layer: Layer, x, residual=None, out=None, idx=None
                                           _ptr(ws, None, "ws"), ws.numel(), _stream()),
            "moe_layer_forward_batched")
     return out, idx, w
+
+
+def gdn_recurrent_step(state, q, k, v, alpha, beta, o=None):
+    """One GatedDeltaNet decode step for every head, state [heads][dv][dk] updated in
+    place: returns o [heads][dv]."""
+    heads, dv, dk = state.shape
+    o = o if o is not None else torch.empty(heads, dv, dtype=torch.float32, device=state.device)
+    for t, n, shp in ((q, "q", (heads, dk)), (k, "k", (heads, dk)), (v, "v", (heads, dv)),
+                      (alpha, "alpha", (heads,)), (beta, "beta", (heads,)), (o, "o", (heads, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    _check(_lib.gdn_recurrent_step(_ptr(state, torch.float32, "state"), _ptr(q, torch.float32, "q"),
+                                   _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                                   _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
+                                   _ptr(o, torch.float32, "o"), heads, dk, dv, _stream()), "gdn_recurrent_step")
+    return o
 
 
 def rmsnorm_f32(v, weight, eps=1e-6, out=None):

@@ -300,6 +300,20 @@ int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* 
                     "moe_layer_forward_batched launch");
 }
 
+int gdn_recurrent_step(float* state, const float* q, const float* k, const float* v, const float* alpha,
+                       const float* beta, float* o, int32_t heads, int32_t dk, int32_t dv, void* stream) {
+  if (heads < 0 || dv < 1) return fail(QMOE_ESHAPE, "heads must be >= 0 and dv >= 1");
+  if (dk != 64 && dk != 128 && dk != 256) return fail(QMOE_ESHAPE, "dk must be 64, 128 or 256");
+  if ((int64_t)heads * dv > (int64_t)1 << 30) return fail(QMOE_ESHAPE, "heads * dv too large");
+  if (heads == 0) return QMOE_OK;
+  int rc = check_vec(state, "state");
+  if (rc || (rc = check_vec(q, "q")) || (rc = check_vec(k, "k"))) return rc;
+  if (!v || !alpha || !beta || !o) return fail(QMOE_EINVAL, "NULL pointer");
+  return hip_status(qmoe::launch_gdn_step(state, q, k, v, alpha, beta, o, heads, dk, dv,
+                                          static_cast<hipStream_t>(stream)),
+                    "gdn_recurrent_step launch");
+}
+
 int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out, void* stream) {
   if (n < 0) return fail(QMOE_EINVAL, "n must be >= 0");
   if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");

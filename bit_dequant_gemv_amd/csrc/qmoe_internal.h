@@ -51,6 +51,10 @@ hipError_t launch_stack(const qmoe_layer* layers, const float* const* norm_w, in
                         const float* h0, float* out, float* h_all, int32_t* idx, float* w, void* ws,
                         bool persistent, hipStream_t s);
 
+// GatedDeltaNet recurrence, one decode step (gdn.hip); dk in {64, 128, 256}
+hipError_t launch_gdn_step(float* S, const float* q, const float* k, const float* v, const float* alpha,
+                           const float* beta, float* o, int heads, int dk, int dv, hipStream_t s);
+
 // batched decode (batched.hip)
 size_t batched_workspace_bytes(const qmoe_layer& L, int T);
 hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float* residual,

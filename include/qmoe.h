@@ -228,6 +228,25 @@ int moe_layer_forward_batched(const qmoe_layer* L, const float* x, const float* 
 size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t T);
 
 /*
+ * One decode step of the GatedDeltaNet recurrence for every head ([PK] "Accelerate
+ * BLAS 활용": per linear-attention layer, 64 heads of a 128x128 state updated by a
+ * scale, a matrix-vector product and a rank-1 update).  With the state S of a head
+ * as [dk][dv] (S^T k recalls the value stored at key k):
+ *   S <- alpha S;  u = S^T k;  S <- S + k (beta (v - u))^T;  o = S^T q.
+ *   state: device float [heads][dv][dk], updated in place; row j of head h holds
+ *          column j of that head's S (contiguous over the keys), 16-byte aligned;
+ *   q, k: device float [heads][dk] (16-byte aligned); v: device float [heads][dv];
+ *   alpha, beta: device float [heads]; o: device float [heads][dv] (written).
+ *   dk: 64, 128 or 256; dv >= 1; heads >= 0 (0: nothing is done).
+ * q, k, v and the gates are taken as given: projections, normalisation and the
+ * gates' nonlinearities come before the recurrence.  Errors: QMOE_ESHAPE for a bad
+ * shape, QMOE_EINVAL / QMOE_EALIGN for a missing or misaligned pointer.
+ */
+int gdn_recurrent_step(float* state, const float* q, const float* k, const float* v,
+                       const float* alpha, const float* beta, float* o, int32_t heads,
+                       int32_t dk, int32_t dv, void* stream);
+
+/*
  * RMSNorm ([PK] Metal shaders: two-stage RMS normalisation):
  *   out = v / sqrt(mean(v^2) + eps) * w;  v, w, out: device float [n]; out may alias v.
  */

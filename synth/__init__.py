@@ -47,6 +47,7 @@ K_GATE_CODES, K_UP_CODES, K_DOWN_CODES = 0, 1, 2
 K_GATE_SCALE, K_UP_SCALE, K_DOWN_SCALE = 3, 4, 5
 K_GATE_BIAS, K_UP_BIAS, K_DOWN_BIAS = 6, 7, 8
 K_ROUTER, K_SHARED_GATE, K_X, K_NORM_W = 9, 10, 11, 12
+K_GDN_STATE, K_GDN_Q, K_GDN_K, K_GDN_V, K_GDN_ALPHA, K_GDN_BETA = 13, 14, 15, 16, 17, 18
 
 # distributions of the synthetic workload
 SCALE_LO, SCALE_HI = 0.001, 0.02     # bf16 scale ~ U(0.001, 0.02)
@@ -55,6 +56,9 @@ ROUTER_SIGMA = 0.02                  # bf16 router ~ N(0, 0.02)
 SHARED_GATE_SIGMA = 0.02             # bf16 shared-expert gate vector ~ N(0, 0.02)
 X_SIGMA = 1.0                        # fp32 activations ~ N(0, 1)
 NORM_LO, NORM_HI = 0.9, 1.1          # fp32 RMSNorm weight ~ U(0.9, 1.1)
+GDN_STATE_SIGMA = 0.1                # GatedDeltaNet state ~ N(0, 0.1)
+GDN_ALPHA_LO, GDN_ALPHA_HI = 0.9, 1.0  # decay gate ~ U(0.9, 1)
+GDN_BETA_LO, GDN_BETA_HI = 0.0, 1.0    # write strength ~ U(0, 1)
 
 _M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
 _W0, _W1 = 0x9E3779B9, 0xBB67AE85
@@ -192,6 +196,27 @@ def activations(seed: int, token: int, H: int) -> np.ndarray:
 
 def norm_weight(seed: int, layer: int, H: int) -> np.ndarray:
     return uniform_f32(seed, tensor_id(K_NORM_W, 0, layer), H, NORM_LO, NORM_HI)
+
+
+def gdn_state(seed: int, layer: int, heads: int, dk: int, dv: int) -> np.ndarray:
+    """A GatedDeltaNet state, fp32 ~N(0, 0.1), as [heads][dv][dk] (the library's
+    layout: row j of a head holds the values at index j over the keys)."""
+    return normal_f32(seed, tensor_id(K_GDN_STATE, 0, layer), heads * dv * dk,
+                      GDN_STATE_SIGMA).reshape(heads, dv, dk)
+
+
+def gdn_token(seed: int, layer: int, token: int, heads: int, dk: int, dv: int):
+    """Inputs of one recurrence step: q and k ~N(0, 1) scaled to unit length per
+    head, v ~N(0, 1), alpha ~U(0.9, 1), beta ~U(0, 1); all fp32."""
+    t = token % 4096
+    q = normal_f32(seed, tensor_id(K_GDN_Q, t, layer), heads * dk, 1.0).reshape(heads, dk)
+    k = normal_f32(seed, tensor_id(K_GDN_K, t, layer), heads * dk, 1.0).reshape(heads, dk)
+    q = (q / np.linalg.norm(q.astype(np.float64), axis=1, keepdims=True)).astype(np.float32)
+    k = (k / np.linalg.norm(k.astype(np.float64), axis=1, keepdims=True)).astype(np.float32)
+    v = normal_f32(seed, tensor_id(K_GDN_V, t, layer), heads * dv, 1.0).reshape(heads, dv)
+    alpha = uniform_f32(seed, tensor_id(K_GDN_ALPHA, t, layer), heads, GDN_ALPHA_LO, GDN_ALPHA_HI)
+    beta = uniform_f32(seed, tensor_id(K_GDN_BETA, t, layer), heads, GDN_BETA_LO, GDN_BETA_HI)
+    return q, k, v, alpha, beta
 
 
 # --------------------------------------------------------------------------

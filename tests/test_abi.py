@@ -91,6 +91,14 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 512, 516, 2, 16, 16, 256, need2, None) == \
         q.QMOE_EALIGN
     assert lib.rmsnorm_f32(16, 16, -1.0, 4, 16, None) == q.QMOE_EINVAL
+    # GatedDeltaNet step: shapes, pointers (heads == 0 is a no-op: no launch)
+    assert lib.gdn_recurrent_step(256, 256, 256, 256, 256, 256, 256, 64, 100, 128, None) == q.QMOE_ESHAPE
+    assert lib.gdn_recurrent_step(256, 256, 256, 256, 256, 256, 256, 64, 128, 0, None) == q.QMOE_ESHAPE
+    assert lib.gdn_recurrent_step(256, 256, 256, 256, 256, 256, 256, -1, 128, 128, None) == q.QMOE_ESHAPE
+    assert lib.gdn_recurrent_step(None, None, None, None, None, None, None, 0, 128, 128, None) == q.QMOE_OK
+    assert lib.gdn_recurrent_step(None, 256, 256, 256, 256, 256, 256, 64, 128, 128, None) == q.QMOE_EINVAL
+    assert lib.gdn_recurrent_step(264, 256, 256, 256, 256, 256, 256, 64, 128, 128, None) == q.QMOE_EALIGN
+    assert lib.gdn_recurrent_step(256, 256, 256, None, 256, 256, 256, 64, 128, 128, None) == q.QMOE_EINVAL
     assert lib.qmoe_workspace_bytes(ctypes.byref(L), 0) == 0
     # stack: no layers, shapes that differ between layers, a short workspace
     Ls = (q.LayerC * 2)(L, L)

@@ -501,3 +501,49 @@ def test_stack_parity(q):
         r = _rel(h.cpu().numpy(), hr)
         say("  token", tok, "stack rel_l2", r)
         assert r <= TOL and r <= TIGHT
+
+
+# ---------------------------------------------------------------------------
+# GatedDeltaNet recurrence (one decode step per call, state updated in place)
+# ---------------------------------------------------------------------------
+
+GDN_CASES = [  # (heads, dk, dv, steps) -- ragged column counts, every dk, the model's full size
+    (3, 64, 5, 3), (2, 128, 7, 3), (1, 256, 3, 3), (5, 128, 1, 2), (64, 128, 128, 4),
+]
+
+
+@pytest.mark.parametrize("heads,dk,dv,steps", GDN_CASES)
+def test_gdn_step_parity(q, heads, dk, dv, steps):
+    say("gdn", heads, dk, dv, steps)
+    seed = 1005
+    S0 = synth.gdn_state(seed, 0, heads, dk, dv)            # [heads][dv][dk]
+    state = torch.from_numpy(S0).cuda()
+    Sref = S0.transpose(0, 2, 1).astype(np.float64)         # the oracle's [heads][dk][dv]
+    for t in range(steps):
+        qq, kk, vv, al, be = synth.gdn_token(seed, 0, t, heads, dk, dv)
+        o = q.gdn_recurrent_step(state, *(torch.from_numpy(a).cuda() for a in (qq, kk, vv, al, be)))
+        Sref, oref = oracle.gdn_step(Sref, qq, kk, vv, al, be)
+        torch.cuda.synchronize()
+        rs = _rel(state.cpu().numpy().transpose(0, 2, 1), Sref)
+        ro = _rel(o.cpu().numpy(), oref)
+        say("  step", t, "state rel_l2", rs, "o rel_l2", ro)
+        assert rs <= 1e-5 and ro <= 1e-5
+
+
+def test_gdn_zero_heads_and_untouched_tail(q):
+    """heads = 0 does nothing; a step writes only the state and o it owns (guard
+    words around both stay as they were)."""
+    st = torch.full((2, 3, 64), 7.0, device="cuda")
+    o = q.gdn_recurrent_step(st[:0], *(torch.zeros(s, device="cuda") for s in ((0, 64), (0, 64), (0, 3), (0,), (0,))))
+    assert o.numel() == 0 and bool((st == 7.0).all())
+    big = torch.full((2 * 3 * 64 + 64,), -1.0, device="cuda")
+    state = big[:2 * 3 * 64].view(2, 3, 64)
+    state.fill_(0.5)
+    ob = torch.full((2 * 3 + 16,), -2.0, device="cuda")
+    qq, kk, vv, al, be = synth.gdn_token(1005, 1, 0, 2, 64, 3)
+    q.gdn_recurrent_step(state, *(torch.from_numpy(a).cuda() for a in (qq, kk, vv, al, be)), o=ob[:6].view(2, 3))
+    torch.cuda.synchronize()
+    assert bool((big[2 * 3 * 64:] == -1.0).all()) and bool((ob[6:] == -2.0).all())
+    Sref, oref = oracle.gdn_step(np.full((2, 64, 3), 0.5), qq, kk, vv, al, be)
+    assert _rel(state.cpu().numpy().transpose(0, 2, 1), Sref) <= 1e-5
+    assert _rel(ob[:6].cpu().numpy().reshape(2, 3), oref) <= 1e-5
