@@ -38,6 +38,10 @@ Readings of the pages where they are silent (each listed in the design notes):
 * GatedDeltaNet: the pages name a scale, a matrix-vector product and a rank-1
   update of a 128x128 state per head; read as the delta rule with a decay gate
   (``gdn_step``), with q, k, v and the two gates given.
+* Full attention: the pages name Q@K^T, softmax, scores@V and RoPE.  Read as one
+  decode token of grouped-query attention with scale 1/sqrt(D) over a key/value
+  cache, rotate-half RoPE on the first rot_dim dimensions of q and k
+  (``attn_decode``).
 
 Parity status of each function is stated in its docstring; every function here
 is pinned by a test in ``tests/test_oracle_pins.py`` against hand-built cases,
@@ -402,6 +406,52 @@ def gdn_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, alpha: 
         S[h] = S[h] + np.outer(k[h], beta[h] * (v[h] - u))
         o[h] = S[h].T @ q[h]
     return S, o
+
+
+# --------------------------------------------------------------------------
+# Full-attention decode   ([PK] Metal shaders: GPU attention -- Q@K^T, softmax,
+# scores@V -- and RoPE; architecture: 15 of the 60 layers are full attention)
+# --------------------------------------------------------------------------
+
+def rope(x: np.ndarray, pos: int, theta: float, rot_dim: int) -> np.ndarray:
+    """Rotary position embedding of every row of x ([rows][D]) at position pos:
+    the first rot_dim dimensions are split in halves (a, b) and each pair
+    (a_i, b_i) is rotated by the angle pos * theta^(-2i/rot_dim); the other
+    dimensions pass through."""
+    x = np.array(x, dtype=np.float64)
+    half = rot_dim // 2
+    ang = pos * theta ** (-2.0 * np.arange(half) / rot_dim)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half].copy(), x[..., half:rot_dim].copy()
+    x[..., :half] = a * c - b * s
+    x[..., half:rot_dim] = b * c + a * s
+    return x
+
+
+def attn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, K: np.ndarray, V: np.ndarray,
+                pos: int, theta: float, rot_dim: int):
+    """One decode token of grouped-query attention over a key/value cache.
+
+    q: [Hq][D]; k, v: [Hkv][D] (this token's); K, V: [Hkv][T][D] caches with
+    T > pos.  q and k are rotated at position pos, the rotated k and v go to row
+    pos of the caches, and query head h attends to rows 0..pos of KV head
+    h // (Hq / Hkv): o_h = sum_t softmax_t(q_h . K_t / sqrt(D)) V_t.
+    Returns (o [Hq][D], K', V')."""
+    q = rope(q, pos, theta, rot_dim)
+    kr = rope(k, pos, theta, rot_dim)
+    K = np.array(K, dtype=np.float64)
+    V = np.array(V, dtype=np.float64)
+    K[:, pos] = kr
+    V[:, pos] = np.asarray(v, dtype=np.float64)
+    hq, D = q.shape
+    group = hq // K.shape[0]
+    o = np.zeros((hq, D))
+    for h in range(hq):
+        g = h // group
+        s = K[g, :pos + 1] @ q[h] / math.sqrt(D)
+        p = np.exp(s - s.max())
+        o[h] = (p / p.sum()) @ V[g, :pos + 1]
+    return o, K, V
 
 
 # --------------------------------------------------------------------------

@@ -508,3 +508,81 @@ def test_gdn_steps_compose():
         d = [b[t] * (vs[t][j] - rec[j]) for j in range(dv)]
         M = [[M[i][j] + ks[t][i] * d[j] for j in range(dv)] for i in range(dk)]
     np.testing.assert_allclose(St[0], np.array(M), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# RoPE and full-attention decode
+# --------------------------------------------------------------------------
+
+def test_rope_hand_case_and_pass_through():
+    """D = 4, rot_dim = 2: the pair (x0, x1) turns by pos radians (theta^0 = 1),
+    x2 and x3 pass through; pos = 0 is the identity."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    r = oracle.rope(x, 3, 10000.0, 2)
+    c, s = math.cos(3.0), math.sin(3.0)
+    np.testing.assert_allclose(r[0], [c - 2 * s, 2 * c + s, 3.0, 4.0], rtol=1e-15)
+    np.testing.assert_array_equal(oracle.rope(x, 0, 10000.0, 4), x)
+
+
+def test_rope_second_frequency_by_hand():
+    """rot_dim = 4, theta = 100: pair 1 is (x1, x3) and turns by pos * 100^(-1/2)."""
+    x = np.array([[0.0, 1.0, 0.0, 0.0]])
+    r = oracle.rope(x, 5, 100.0, 4)
+    a = 5 * 0.1
+    np.testing.assert_allclose(r[0], [0.0, math.cos(a), 0.0, math.sin(a)], atol=1e-15)
+
+
+def test_rope_is_relative():
+    """Rotations preserve length, and rope(q, m) . rope(k, n) depends on m - n only."""
+    rng = np.random.default_rng(21)
+    q, k = rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    for m, n in ((7, 3), (40, 36), (4, 0)):
+        d1 = float(oracle.rope(q, m, 500.0, 16)[0] @ oracle.rope(k, n, 500.0, 16)[0])
+        d0 = float(oracle.rope(q, m - n, 500.0, 16)[0] @ k[0])
+        assert d1 == pytest.approx(d0, rel=1e-12)
+        assert np.linalg.norm(oracle.rope(q, m, 500.0, 12)) == pytest.approx(np.linalg.norm(q), rel=1e-14)
+
+
+def test_attn_single_key_returns_its_value():
+    """At pos = 0 the only key is the token's own: o = v for every query head."""
+    rng = np.random.default_rng(22)
+    q, k, v = rng.standard_normal((4, 8)), rng.standard_normal((2, 8)), rng.standard_normal((2, 8))
+    o, K, V = oracle.attn_decode(q, k, v, np.zeros((2, 5, 8)), np.zeros((2, 5, 8)), 0, 1e4, 8)
+    for h in range(4):
+        np.testing.assert_allclose(o[h], v[h // 2], rtol=1e-15)
+    np.testing.assert_array_equal(V[:, 0], v)
+    np.testing.assert_allclose(K[:, 0], k, rtol=1e-15)   # rotation at position 0 is the identity
+
+
+def test_attn_equal_keys_average_the_values():
+    """Keys identical to the token's rotated key: uniform weights, o = mean of V[0..pos]."""
+    rng = np.random.default_rng(23)
+    D, pos = 8, 4
+    q, k, v = rng.standard_normal((2, D)), rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    kr = oracle.rope(k, pos, 1e4, D)
+    K = np.repeat(kr[:, None, :], 6, axis=1)
+    V = rng.standard_normal((1, 6, D))
+    o, _, V2 = oracle.attn_decode(q, k, v, K, V, pos, 1e4, D)
+    np.testing.assert_allclose(o[0], V2[0, :pos + 1].mean(axis=0), rtol=1e-12)
+    np.testing.assert_allclose(o[1], o[0], rtol=1e-12)
+
+
+def test_attn_brute_force_with_explicit_softmax():
+    """A tiny case summed by hand with math.exp (grouping 3:1, partial rotation)."""
+    rng = np.random.default_rng(24)
+    Hq, Hkv, D, T, pos = 3, 1, 4, 5, 3
+    q, k, v = rng.standard_normal((Hq, D)), rng.standard_normal((Hkv, D)), rng.standard_normal((Hkv, D))
+    K, V = rng.standard_normal((Hkv, T, D)), rng.standard_normal((Hkv, T, D))
+    o, K2, V2 = oracle.attn_decode(q, k, v, K, V, pos, 50.0, 2)
+    c, s = math.cos(pos), math.sin(pos)
+    def rot(x):
+        return [x[0] * c - x[1] * s, x[1] * c + x[0] * s, x[2], x[3]]
+    keys = [list(K[0, t]) for t in range(pos)] + [rot(k[0])]
+    vals = [list(V[0, t]) for t in range(pos)] + [list(v[0])]
+    for h in range(Hq):
+        qh = rot(q[h])
+        sc = [sum(a * b for a, b in zip(qh, key)) / 2.0 for key in keys]
+        w = [math.exp(x - max(sc)) for x in sc]
+        ref = [sum(w[t] * vals[t][d] for t in range(pos + 1)) / sum(w) for d in range(D)]
+        np.testing.assert_allclose(o[h], ref, rtol=1e-12)
+    np.testing.assert_array_equal(K2[0, pos + 1:], K[0, pos + 1:])   # rows past pos untouched
