@@ -15,6 +15,9 @@ Workloads (all weights 4-bit unless noted; H = 4096, I = 1024, group 64):
   --config 5            one GatedDeltaNet recurrence step (64 heads x 128x128
                         fp32 state) on a ring of 128 resident states; a step is
                         one call
+  --config 6            one full-attention decode token (32 query heads over 2 KV
+                        heads of 256, context 8192, fp32 caches) on a ring of 16
+                        caches; a step is one call
 Inputs are synthetic (seeded Philox streams generated in HBM); weights and
 activations are resident in HBM before the timed region starts.  Steps are
 enqueued as replays of HIP graphs, so the host never synchronises inside the
@@ -366,6 +369,61 @@ def run_gdn_bench(args, torch, q, synth):
                        "state_ring": ring, "state_ring_MB": ring * heads * dk * dv * 4 >> 20}}
 
 
+def run_attn_bench(args, torch, q, synth):
+    """One full-attention decode token (RoPE, cache append, grouped-query attention)
+    at context 8192: 32 query heads over 2 KV heads of 256, fp32 caches, on a ring of
+    16 layers' caches (512 MB, more than the last-level cache)."""
+    import numpy as np
+    Hq, Hkv, D, T, ring, rot, theta = 32, 2, 256, 8192, 16, 64, 1e7
+    seed = 1006
+    KC = torch.empty(ring, Hkv, T, D, dtype=torch.float32, device="cuda")
+    VC = torch.empty_like(KC)
+    synth.fill_normal_f32(KC, seed, synth.tensor_id(synth.K_ATTN_KCACHE, 0, 0), 1.0)
+    synth.fill_normal_f32(VC, seed, synth.tensor_id(synth.K_ATTN_VCACHE, 0, 0), 1.0)
+    toks = [synth.attn_token(seed, 0, t, Hq, Hkv, D) for t in range(16)]
+    Qs, Ks, Vs = (torch.from_numpy(np.stack([t[i] for t in toks])).cuda() for i in range(3))
+    o = torch.empty(Hq, D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.qmoe_attn_workspace_bytes(Hq, Hkv, D, T), dtype=torch.uint8, device="cuda")
+    calls = [(lambda i=i: q.attn_decode_step(Qs[i % 16], Ks[i % 16], Vs[i % 16], KC[i % ring], VC[i % ring],
+                                             T - 1, theta, rot, o=o, ws=ws)) for i in range(ring)]
+    steps = max(1, args.steps)
+    dt = timed_steps(torch, calls, steps, args.warmup, ring)
+    if not bool(torch.isfinite(o).all()):
+        raise RuntimeError("attention output is not finite")
+    per_step = 2 * Hkv * T * D * 4 + 2 * Hq * D * 4 + 2 * Hkv * D * 4
+    launch_s = dt / steps
+    roof = {"bound": "hbm", "achieved": round(per_step / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(per_step / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles("k_attn_part")}
+    extra = {"kernel": "attn_decode_step (k_rope_append, k_attn_part<256>, k_attn_combine<256>)",
+             "bytes_per_step": per_step, "avg_step_us": round(launch_s * 1e6, 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_attn(seed, Hq, Hkv, D, T, rot, theta, args.cpu_seconds)
+    return {"value": steps / dt, "unit": "decode tokens/s (one attention layer)", "steps": steps, "dt": dt,
+            "roof": roof, "extra": extra, "cpu": cpu, "workload": "attn_decode_32q_2kv_d256_ctx8192",
+            "bits": None, "metric": "full-attention decode tokens/s per layer (GQA 32/2, D 256, context 8192, fp32 cache), batch 1",
+            "config": {"workload": "attn_decode_32q_2kv_d256_ctx8192", "q_heads": Hq, "kv_heads": Hkv,
+                       "head_dim": D, "context": T, "rot_dim": rot, "theta": theta, "cache_ring": ring,
+                       "cache_ring_MB": ring * 2 * Hkv * T * D * 4 >> 20}}
+
+
+def cpu_oracle_attn(seed, Hq, Hkv, D, T, rot, theta, target_s):
+    """The oracle's attention decode (float64, numpy) on the host, repeated for about
+    target_s seconds on one cache."""
+    import oracle
+    import synth
+    K, V = synth.attn_cache(seed, 0, Hkv, T, D)
+    toks = [synth.attn_token(seed, 0, t, Hq, Hkv, D) for t in range(4)]
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        oracle.attn_decode(*toks[n % 4], K, V, T - 1, theta, rot)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "decode tokens/s (one attention layer)",
+            "cores": blas_threads(), "kind": "oracle", "sample": f"{n} tokens at context {T}"}
+
+
 def cpu_oracle_gdn(seed, heads, dk, dv, target_s):
     """The oracle's recurrence step (float64, numpy) on the host, repeated for about
     target_s seconds on one state."""
@@ -518,7 +576,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16384)
     ap.add_argument("--warmup", type=int, default=1024)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--persistent", action="store_true",
@@ -556,6 +614,8 @@ def main():
         r = run_stack_bench(args, torch, q, synth)
     elif args.config == 5:
         r = run_gdn_bench(args, torch, q, synth)
+    elif args.config == 6:
+        r = run_attn_bench(args, torch, q, synth)
     else:
         r = run_batched_bench(args, torch, q, synth)
     r["extra"].update(extra0)

@@ -77,6 +77,9 @@ _SIGS = {
     "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
     "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
     "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "attn_decode_step": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz,
+                          _vp], ctypes.c_int),
+    "qmoe_attn_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "qmoe_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "qmoe_last_error": ([], ctypes.c_char_p),
 }
@@ -356,6 +359,31 @@ def gdn_recurrent_step(state, q, k, v, alpha, beta, o=None):
                                    _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
                                    _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
                                    _ptr(o, torch.float32, "o"), heads, dk, dv, _stream()), "gdn_recurrent_step")
+    return o
+
+
+def qmoe_attn_workspace_bytes(Hq: int, Hkv: int, D: int, Tmax: int) -> int:
+    return int(_lib.qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax))
+
+
+def attn_decode_step(q, k, v, k_cache, v_cache, pos, theta=1e7, rot_dim=None, o=None, ws=None):
+    """One decode token of grouped-query attention with RoPE: writes row pos of the
+    caches ([Hkv][Tmax][D]) and returns o [Hq][D]."""
+    Hq, D = q.shape
+    Hkv, Tmax, D2 = k_cache.shape
+    rot_dim = D if rot_dim is None else rot_dim
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(k.shape) != (Hkv, D) \
+            or tuple(v.shape) != (Hkv, D):
+        raise ValueError("q [Hq][D], k and v [Hkv][D], caches [Hkv][Tmax][D]")
+    o = o if o is not None else torch.empty(Hq, D, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(256, qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax)), dtype=torch.uint8,
+                         device=q.device)
+    _check(_lib.attn_decode_step(_ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"),
+                                 _ptr(v, torch.float32, "v"), _ptr(k_cache, torch.float32, "k_cache"),
+                                 _ptr(v_cache, torch.float32, "v_cache"), Hq, Hkv, D, Tmax, pos, theta,
+                                 rot_dim, _ptr(o, torch.float32, "o"), _ptr(ws, None, "ws"), ws.numel(),
+                                 _stream()), "attn_decode_step")
     return o
 
 

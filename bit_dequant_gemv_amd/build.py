@@ -55,7 +55,7 @@ def _library(srcs, out, extra, verbose, jobs):
 
 def build_qmoe(verbose=False, jobs=None):
     csrc = os.path.join(HERE, "csrc")
-    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip")]
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip", "attn.hip")]
     return _library(srcs, os.path.join(HERE, "libqmoe.so"),
                     ["-I", os.path.join(ROOT, "include"), "-I", csrc], verbose,
                     jobs or min(8, os.cpu_count() or 4))

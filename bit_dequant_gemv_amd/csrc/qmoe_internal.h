@@ -55,6 +55,12 @@ hipError_t launch_stack(const qmoe_layer* layers, const float* const* norm_w, in
 hipError_t launch_gdn_step(float* S, const float* q, const float* k, const float* v, const float* alpha,
                            const float* beta, float* o, int heads, int dk, int dv, hipStream_t s);
 
+// full-attention decode (attn.hip); D in {64, 128, 256}, Hq / Hkv <= 16
+size_t attn_workspace_bytes(int Hq, int Hkv, int D, int Tmax);
+hipError_t launch_attn_decode(const float* q, const float* k, const float* v, float* kc, float* vc,
+                              int Hq, int Hkv, int D, int Tmax, int pos, float theta, int rot_dim,
+                              float* o, void* ws, hipStream_t s);
+
 // batched decode (batched.hip)
 size_t batched_workspace_bytes(const qmoe_layer& L, int T);
 hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float* residual,

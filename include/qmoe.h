@@ -247,6 +247,33 @@ int gdn_recurrent_step(float* state, const float* q, const float* k, const float
                        int32_t dk, int32_t dv, void* stream);
 
 /*
+ * One decode token of grouped-query attention with rotary position embedding
+ * ([PK] Metal shaders: GPU attention -- Q@K^T, softmax, scores@V -- and RoPE;
+ * architecture: 15 of the 60 layers are full attention):
+ *   q, k <- rope(q, pos), rope(k, pos): on the first rot_dim dimensions, the pairs
+ *           (x_i, x_{i + rot_dim/2}) turn by pos * theta^(-2i/rot_dim); the rest pass;
+ *   k_cache[g][pos], v_cache[g][pos] <- k[g], v[g];
+ *   o[h] = sum_{t <= pos} softmax_t(q[h] . k_cache[g][t] / sqrt(D)) v_cache[g][t],
+ *          g = h / (Hq / Hkv).
+ *   q: device float [Hq][D]; k, v: device float [Hkv][D] (this token's, before RoPE);
+ *   k_cache, v_cache: device float [Hkv][Tmax][D], row pos written, rows < pos read;
+ *   o: device float [Hq][D] (written); all 16-byte aligned.
+ *   D: 64, 128 or 256; Hq a multiple of Hkv with Hq / Hkv <= 16; 0 <= pos < Tmax;
+ *   rot_dim even, 0..D; theta > 0.
+ *   ws: at least qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax) bytes, 256-byte aligned
+ *   (scratch: no state is kept between calls).
+ * Errors: QMOE_ESHAPE for a bad shape or position, QMOE_EINVAL / QMOE_EALIGN /
+ * QMOE_EWORKSPACE for bad pointers, theta or workspace.
+ */
+int attn_decode_step(const float* q, const float* k, const float* v, float* k_cache,
+                     float* v_cache, int32_t Hq, int32_t Hkv, int32_t D, int32_t Tmax, int32_t pos,
+                     float theta, int32_t rot_dim, float* o, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes for attn_decode_step (0 for a bad shape). */
+size_t qmoe_attn_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t Tmax);
+
+/*
  * RMSNorm ([PK] Metal shaders: two-stage RMS normalisation):
  *   out = v / sqrt(mean(v^2) + eps) * w;  v, w, out: device float [n]; out may alias v.
  */

@@ -48,6 +48,7 @@ K_GATE_SCALE, K_UP_SCALE, K_DOWN_SCALE = 3, 4, 5
 K_GATE_BIAS, K_UP_BIAS, K_DOWN_BIAS = 6, 7, 8
 K_ROUTER, K_SHARED_GATE, K_X, K_NORM_W = 9, 10, 11, 12
 K_GDN_STATE, K_GDN_Q, K_GDN_K, K_GDN_V, K_GDN_ALPHA, K_GDN_BETA = 13, 14, 15, 16, 17, 18
+K_ATTN_Q, K_ATTN_K, K_ATTN_V, K_ATTN_KCACHE, K_ATTN_VCACHE = 19, 20, 21, 22, 23
 
 # distributions of the synthetic workload
 SCALE_LO, SCALE_HI = 0.001, 0.02     # bf16 scale ~ U(0.001, 0.02)
@@ -203,6 +204,22 @@ def gdn_state(seed: int, layer: int, heads: int, dk: int, dv: int) -> np.ndarray
     layout: row j of a head holds the values at index j over the keys)."""
     return normal_f32(seed, tensor_id(K_GDN_STATE, 0, layer), heads * dv * dk,
                       GDN_STATE_SIGMA).reshape(heads, dv, dk)
+
+
+def attn_cache(seed: int, layer: int, Hkv: int, T: int, D: int):
+    """Key and value caches [Hkv][T][D], fp32 ~N(0, 1)."""
+    K = normal_f32(seed, tensor_id(K_ATTN_KCACHE, 0, layer), Hkv * T * D, 1.0).reshape(Hkv, T, D)
+    V = normal_f32(seed, tensor_id(K_ATTN_VCACHE, 0, layer), Hkv * T * D, 1.0).reshape(Hkv, T, D)
+    return K, V
+
+
+def attn_token(seed: int, layer: int, token: int, Hq: int, Hkv: int, D: int):
+    """q [Hq][D], k and v [Hkv][D] of one decode token, fp32 ~N(0, 1)."""
+    t = token % 4096
+    q = normal_f32(seed, tensor_id(K_ATTN_Q, t, layer), Hq * D, 1.0).reshape(Hq, D)
+    k = normal_f32(seed, tensor_id(K_ATTN_K, t, layer), Hkv * D, 1.0).reshape(Hkv, D)
+    v = normal_f32(seed, tensor_id(K_ATTN_V, t, layer), Hkv * D, 1.0).reshape(Hkv, D)
+    return q, k, v
 
 
 def gdn_token(seed: int, layer: int, token: int, heads: int, dk: int, dv: int):

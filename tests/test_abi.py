@@ -91,6 +91,17 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.moe_layer_forward_batched(ctypes.byref(L), 256, 512, 516, 2, 16, 16, 256, need2, None) == \
         q.QMOE_EALIGN
     assert lib.rmsnorm_f32(16, 16, -1.0, 4, 16, None) == q.QMOE_EINVAL
+    # attention decode: shapes, position, rotation, workspace
+    na = lib.qmoe_attn_workspace_bytes(32, 2, 256, 4096)
+    assert na > 0 and lib.qmoe_attn_workspace_bytes(32, 2, 100, 4096) == 0
+    assert lib.qmoe_attn_workspace_bytes(34, 2, 256, 4096) == 0 and lib.qmoe_attn_workspace_bytes(34, 1, 256, 8) == 0
+    def attn(Hq=32, Hkv=2, D=256, Tmax=4096, pos=5, theta=1e7, rot=64, ws=256, wsb=None):
+        return lib.attn_decode_step(256, 256, 256, 256, 256, Hq, Hkv, D, Tmax, pos, theta, rot, 256, ws,
+                                    na if wsb is None else wsb, None)
+    assert attn(pos=4096) == q.QMOE_ESHAPE and attn(pos=-1) == q.QMOE_ESHAPE
+    assert attn(rot=3) == q.QMOE_ESHAPE and attn(rot=258) == q.QMOE_ESHAPE
+    assert attn(theta=0.0) == q.QMOE_EINVAL and attn(Hq=33) == q.QMOE_ESHAPE
+    assert attn(wsb=na - 1) == q.QMOE_EWORKSPACE and attn(ws=272) == q.QMOE_EALIGN
     # GatedDeltaNet step: shapes, pointers (heads == 0 is a no-op: no launch)
     assert lib.gdn_recurrent_step(256, 256, 256, 256, 256, 256, 256, 64, 100, 128, None) == q.QMOE_ESHAPE
     assert lib.gdn_recurrent_step(256, 256, 256, 256, 256, 256, 256, 64, 128, 0, None) == q.QMOE_ESHAPE

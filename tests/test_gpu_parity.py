@@ -547,3 +547,48 @@ def test_gdn_zero_heads_and_untouched_tail(q):
     Sref, oref = oracle.gdn_step(np.full((2, 64, 3), 0.5), qq, kk, vv, al, be)
     assert _rel(state.cpu().numpy().transpose(0, 2, 1), Sref) <= 1e-5
     assert _rel(ob[:6].cpu().numpy().reshape(2, 3), oref) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# full-attention decode (RoPE, cache append, grouped-query attention)
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [  # (Hq, Hkv, D, Tmax, pos, rot_dim, theta) -- ragged tiles, one key, 16:1 groups,
+    (4, 2, 64, 40, 37, 64, 1e4),        # partial and no rotation, the full 4096-key context
+    (3, 1, 128, 100, 0, 128, 1e4), (16, 1, 256, 300, 299, 64, 1e7), (8, 8, 128, 65, 64, 0, 1e4),
+    (32, 2, 256, 4096, 4095, 64, 1e7),
+]
+
+
+def _attn_check(q, Hq, Hkv, D, Tmax, pos, rot, theta, tokens, seed=1006):
+    K0, V0 = synth.attn_cache(seed, 0, Hkv, Tmax, D)
+    kc, vc = torch.from_numpy(K0).cuda(), torch.from_numpy(V0).cuda()
+    kc[:, pos + 1:] = float("nan")  # rows past the token must never be read
+    vc[:, pos + 1:] = float("nan")
+    ws = torch.empty(q.qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax), dtype=torch.uint8, device="cuda")
+    for i in range(tokens):
+        p = pos + i
+        Kh, Vh = kc.cpu().numpy(), vc.cpu().numpy()  # the caches as the GPU holds them before the token
+        qq, kk, vv = synth.attn_token(seed, 0, p, Hq, Hkv, D)
+        o = q.attn_decode_step(*(torch.from_numpy(a).cuda() for a in (qq, kk, vv)), kc, vc, p, theta, rot, ws=ws)
+        torch.cuda.synchronize()
+        oref, Kref, Vref = oracle.attn_decode(qq, kk, vv, np.nan_to_num(Kh), np.nan_to_num(Vh), p, theta, rot)
+        r = _rel(o.cpu().numpy(), oref)
+        say("  pos", p, "o rel_l2", r)
+        assert r <= 1e-4
+        K2, V2 = kc.cpu().numpy(), vc.cpu().numpy()
+        assert _rel(K2[:, p], Kref[:, p]) <= 1e-6 and np.array_equal(V2[:, p], vv)
+        assert np.array_equal(K2[:, :p], Kh[:, :p]) and np.array_equal(V2[:, :p], Vh[:, :p])
+        assert np.isnan(K2[:, p + 1:]).all() and np.isnan(V2[:, p + 1:]).all()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,Tmax,pos,rot,theta", ATTN_CASES)
+def test_attn_decode_parity(q, Hq, Hkv, D, Tmax, pos, rot, theta):
+    say("attention decode", Hq, Hkv, D, Tmax, pos, rot, theta)
+    _attn_check(q, Hq, Hkv, D, Tmax, pos, rot, theta, tokens=1)
+
+
+def test_attn_decode_consecutive_tokens(q):
+    """Three tokens in a row: each appends its key and value and sees the earlier ones."""
+    say("attention decode, 3 tokens")
+    _attn_check(q, 8, 2, 128, 200, 60, 128, 1e6, tokens=3)
