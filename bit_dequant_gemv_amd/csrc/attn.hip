@@ -19,7 +19,10 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kTK = 32;  // keys per LDS tile
+// keys per LDS tile (16-key tiles, three workgroups per CU, measured slower: 26.8 against
+// 26.0 us at context 8192)
+constexpr int kTK = 32;
+constexpr int kSPL = 64 / kTK;  // lanes per key in the score phase, each summing D / kSPL dims
 constexpr int kMaxSplit = 2048;  // splits per head: at most ceil(256 / Hkv) <= 256, or T / kTK
 
 // a partial result record: acc[D], m, l, padding to a multiple of 16 bytes
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* kc, const float
   const float scale = 1.0f / sqrtf((float)D);
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int kt = lane & 31, kh = lane >> 5;  // score phase: key kt, half kh of the dims
+  const int kt = lane % kTK, kh = lane / kTK;  // score phase: key kt, part kh of the dims
   for (int tb = t0; tb < t1; tb += kTK) {
     const int nk = min(kTK, t1 - tb);
     __syncthreads();  // the previous tile is consumed (and s_q is written)
@@ -95,12 +98,12 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* kc, const float
       reinterpret_cast<float4*>(s_v)[i] = vv;
     }
     __syncthreads();
-    // scores: lane (kt, kh) sums half kh of q_h . K_kt
+    // scores: lane (kt, kh) sums part kh of q_h . K_kt
     float sp = 0.f;
-    const float* kr = s_k + kt * KS + kh * (D / 2);
-    const float* qh = s_q + wv * D + kh * (D / 2);
+    const float* kr = s_k + kt * KS + kh * (D / kSPL);
+    const float* qh = s_q + wv * D + kh * (D / kSPL);
 #pragma unroll 8
-    for (int c = 0; c < D / 2; c += 4) {
+    for (int c = 0; c < D / kSPL; c += 4) {
       const float4 a = *reinterpret_cast<const float4*>(kr + c);
       const float4 b = *reinterpret_cast<const float4*>(qh + c);
       sp = fmaf(a.x, b.x, sp);
@@ -108,17 +111,18 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* kc, const float
       sp = fmaf(a.z, b.z, sp);
       sp = fmaf(a.w, b.w, sp);
     }
-    sp += __shfl_xor(sp, 32);
+#pragma unroll
+    for (int o = 32; o >= kTK; o >>= 1) sp += __shfl_xor(sp, o);
     const float sc = kt < nk ? sp * scale : -INFINITY;
     float tmax = sc;
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+    for (int o = kTK / 2; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
     const float mn = fmaxf(m, tmax);
     const float corr = __expf(m - mn);  // m = -inf on the first tile: 0
     const float p = kt < nk ? __expf(sc - mn) : 0.f;
     float ps = p;
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
+    for (int o = kTK / 2; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
     l = fmaf(l, corr, ps);
     m = mn;
     acc.x *= corr;
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(1024) void k_attn_combine(const float* part, float*
 
 // keys per split: about one workgroup per CU (a workgroup fills a CU's LDS), whole
 // tiles
-constexpr int kWantSplits = 256;
+constexpr int kWantSplits = 256;  // 512 measured slower (30.2 us)
 int attn_chunk(int Hkv, int T) {
   const int64_t want = kWantSplits;
   int64_t c = ((int64_t)T * Hkv + want - 1) / want;
