@@ -1,7 +1,7 @@
 // GatedDeltaNet recurrence, one decode step for every head.
 //
-// The page "flash-moe 소개" (discuss.pytorch.kr), section "Accelerate BLAS 활용",
-// updates a 128x128 state per head (64 heads) in each linear-attention layer with a
+// The page "flash-moe 소개" (discuss.pytorch.kr), section "Accelerate BLAS를 이용한
+// 선형 어텐션 가속", updates a 128x128 state per head (64 heads) in each linear-attention layer with a
 // scale, a matrix-vector product and a rank-1 update; section "Qwen3.5-397B-A17B
 // 모델 아키텍처" puts 45 such layers among the 60.  Per head, with the state S as
 // [dk][dv] (S^T k is the value recalled for the key k):

@@ -229,8 +229,8 @@ size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t T);
 
 /*
  * One decode step of the GatedDeltaNet recurrence for every head ([PK] "Accelerate
- * BLAS 활용": per linear-attention layer, 64 heads of a 128x128 state updated by a
- * scale, a matrix-vector product and a rank-1 update).  With the state S of a head
+ * BLAS를 이용한 선형 어텐션 가속": per linear-attention layer, 64 heads of a 128x128
+ * state updated by a scale, a matrix-vector product and a rank-1 update).  With the state S of a head
  * as [dk][dv] (S^T k recalls the value stored at key k):
  *   S <- alpha S;  u = S^T k;  S <- S + k (beta (v - u))^T;  o = S^T q.
  *   state: device float [heads][dv][dk], updated in place; row j of head h holds

@@ -371,7 +371,8 @@ def moe_stack(layers, h0: np.ndarray, hidden, inter, bits, top_k, eps=1e-6):
 
 
 # --------------------------------------------------------------------------
-# GatedDeltaNet recurrence   ([PK] "Accelerate BLAS 활용" / [GN] "핵심 기술":
+# GatedDeltaNet recurrence   ([PK] "Accelerate BLAS를 이용한 선형 어텐션 가속" /
+# [GN] "핵심 기술", "Accelerate BLAS 활용":
 # the linear-attention layers update a 128x128 state per head, 64 heads, with a
 # scale, a matrix-vector product and a rank-1 update; [PK] architecture: 45 of
 # the 60 layers are GatedDeltaNet layers)
