@@ -395,7 +395,7 @@ def run_attn_bench(args, torch, q, synth):
     roof = {"bound": "hbm", "achieved": round(per_step / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(per_step / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profiles("k_attn_part")}
-    extra = {"kernel": "attn_decode_step (k_rope_append, k_attn_part<256>, k_attn_combine<256>)",
+    extra = {"kernel": "attn_decode_step (k_attn_part<256>, k_attn_combine<256>)",
              "bytes_per_step": per_step, "avg_step_us": round(launch_s * 1e6, 3)}
     cpu = None
     if not args.no_cpu_baseline:

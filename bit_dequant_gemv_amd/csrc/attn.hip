@@ -8,10 +8,10 @@
 //   q, k <- rope(q, pos), rope(k, pos)   (rotate-half on the first rot_dim dims)
 //   K[g][pos], V[g][pos] <- k[g], v[g]
 //   o[h] = sum_{t <= pos} softmax_t(q[h] . K[g][t] / sqrt(D)) V[g][t],  g = h / (Hq/Hkv)
-// Three launches: k_rope_append (rotations, cache rows), k_attn_part (a workgroup
-// per KV head and key range; one wave per query head of the group, so each key and
-// value row is read from HBM once for the whole group; online softmax over tiles of
-// 32 keys staged in LDS), k_attn_combine (the ranges' partial results merged).
+// Two launches: k_attn_part (rotations and cache rows; a workgroup per KV head and
+// key range, one wave per query head of the group, so each key and value row is
+// read from HBM once for the whole group; online softmax over tiles of 32 keys
+// staged in LDS) and k_attn_combine (the ranges' partial results merged).
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -31,66 +31,77 @@ constexpr int rec() {
   return D + 4;
 }
 
-// rows 0..Hq-1: q (rotated into qr); rows Hq..Hq+Hkv-1: this token's k (rotated) and
-// v, written to row pos of the caches.  One thread per dimension.
-__global__ void k_rope_append(const float* q, const float* k, const float* v, float* kc, float* vc,
-                              float* qr, int Hq, int D, int64_t Tmax, int pos, float theta,
-                              int rot_dim) {
-  const int r = blockIdx.x, d = threadIdx.x;
-  const bool isq = r < Hq;
-  const float* x = isq ? q + (int64_t)r * D : k + (int64_t)(r - Hq) * D;
-  const int half = rot_dim / 2;
-  float y = x[d];
-  if (d < rot_dim) {
-    const int i = d < half ? d : d - half;
-    // the angle in double: pos * theta^(-2i/rot_dim) reaches 1e4 rad and more
-    const double ang = (double)pos * pow((double)theta, -2.0 * i / rot_dim);
-    double s, c;
-    sincos(ang, &s, &c);
-    y = d < half ? (float)(x[d] * c - x[d + half] * s) : (float)(x[d] * c + x[d - half] * s);
-  }
-  if (isq) {
-    qr[(int64_t)r * D + d] = y;
-  } else {
-    const int64_t row = ((int64_t)(r - Hq) * Tmax + pos) * D + d;
-    kc[row] = y;
-    vc[row] = v[(int64_t)(r - Hq) * D + d];
-  }
-}
-
 // Partial attention of the G query heads of KV head g over keys [t0, t1): the
 // running max m, the sum of weights l and the weighted sum of values acc[D], in
 // part[h][split][D + 4] = {acc..., m, l, -, -}.  One wave per query head (measured
 // faster than a wave serving four heads, 25.9 against 33.0 us at context 8192, and
 // than waves reading rows straight from memory for all 16 heads, 31.6 us).
+// RoPE and the cache append are done here too: every workgroup takes the rotation
+// angles of position pos (rot_dim / 2 of them, the same for every head) and rotates
+// its group's q rows into LDS; the workgroup whose range holds pos rotates the new
+// k, writes k and v to row pos of the caches and puts them into its tile directly
+// (no other workgroup reads that row in this call).
 template <int D>
-__global__ __launch_bounds__(1024) void k_attn_part(const float* kc, const float* vc, const float* qr,
-                                                    float* part, int G, int64_t Tmax, int T,
-                                                    int chunk, int nsplit) {
+__global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float* knew,
+                                                    const float* vnew, float* kc, float* vc,
+                                                    float* part, int G, int64_t Tmax, int pos,
+                                                    float theta, int rot_dim, int chunk, int nsplit) {
   constexpr int KS = D + 4;  // padded K row in LDS: lanes reading different rows spread over banks
   __shared__ __align__(16) float s_k[kTK * KS];
   __shared__ __align__(16) float s_v[kTK * D];
   __shared__ __align__(16) float s_q[16 * D];
+  __shared__ float s_cs[2][D / 2];                // cos, sin of the rotation pairs
+  __shared__ __align__(16) float s_kn[D], s_vn[D];  // the token's rotated k and its v
   const int g = blockIdx.x, split = blockIdx.y;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = g * G + wv;
   const int nthr = G * 64;
+  const int T = pos + 1;
   const int t0 = split * chunk, t1 = min(T, t0 + chunk);
-  const float* kg = kc + (int64_t)g * Tmax * D;
-  const float* vg = vc + (int64_t)g * Tmax * D;
-  for (int i = threadIdx.x; i < G * D / 4; i += nthr)
-    reinterpret_cast<float4*>(s_q)[i] = reinterpret_cast<const float4*>(qr + (int64_t)g * G * D)[i];
+  const bool owns_pos = t0 <= pos && pos < t1;
+  float* kg = kc + (int64_t)g * Tmax * D;
+  float* vg = vc + (int64_t)g * Tmax * D;
+  const int half = rot_dim / 2;
+  for (int i = threadIdx.x; i < half; i += nthr) {
+    // in double: pos * theta^(-2i/rot_dim) reaches 1e4 rad and more
+    const double ang = (double)pos * pow((double)theta, -2.0 * i / rot_dim);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    s_cs[0][i] = (float)cs;
+    s_cs[1][i] = (float)sn;
+  }
+  __syncthreads();
+  // x_d of a row rotated: pair (d, d + half) for d < half, (d - half, d) below rot_dim
+  auto rot = [&](const float* x, int d) -> float {
+    if (d < half) return x[d] * s_cs[0][d] - x[d + half] * s_cs[1][d];
+    if (d < rot_dim) return x[d] * s_cs[0][d - half] + x[d - half] * s_cs[1][d - half];
+    return x[d];
+  };
+  for (int i = threadIdx.x; i < G * D; i += nthr)
+    s_q[i] = rot(q + (int64_t)(g * G + i / D) * D, i % D);
+  if (owns_pos) {
+    for (int d = threadIdx.x; d < D; d += nthr) {
+      const float kr = rot(knew + (int64_t)g * D, d), vr = vnew[(int64_t)g * D + d];
+      s_kn[d] = kr;
+      s_vn[d] = vr;
+      kg[(int64_t)pos * D + d] = kr;
+      vg[(int64_t)pos * D + d] = vr;
+    }
+  }
   const float scale = 1.0f / sqrtf((float)D);
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int kt = lane % kTK, kh = lane / kTK;  // score phase: key kt, part kh of the dims
   for (int tb = t0; tb < t1; tb += kTK) {
     const int nk = min(kTK, t1 - tb);
-    __syncthreads();  // the previous tile is consumed (and s_q is written)
+    __syncthreads();  // the previous tile is consumed (and s_q, s_kn, s_vn are written)
     for (int i = threadIdx.x; i < kTK * D / 4; i += nthr) {
       const int t = i / (D / 4), c4 = i % (D / 4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (t < nk) {
+      if (tb + t == pos) {  // this token: from LDS (its cache row is written above)
+        kv = reinterpret_cast<const float4*>(s_kn)[c4];
+        vv = reinterpret_cast<const float4*>(s_vn)[c4];
+      } else if (t < nk) {
         kv = reinterpret_cast<const float4*>(kg + (int64_t)(tb + t) * D)[c4];
         vv = reinterpret_cast<const float4*>(vg + (int64_t)(tb + t) * D)[c4];
       }
@@ -226,15 +237,11 @@ hipError_t launch_d(const float* q, const float* k, const float* v, float* kc, f
   const int T = pos + 1, G = Hq / Hkv;
   const int chunk = attn_chunk(Hkv, T);
   const int nsplit = (T + chunk - 1) / chunk;
-  float* qr = ws;
-  float* part = ws + (int64_t)Hq * D;
-  hipLaunchKernelGGL(k_rope_append, dim3(Hq + Hkv), dim3(D), 0, s, q, k, v, kc, vc, qr, Hq, D, Tmax,
-                     pos, theta, rot_dim);
+  float* part = ws;
+  hipLaunchKernelGGL(k_attn_part<D>, dim3(Hkv, nsplit), dim3(G * 64), 0, s, q, k, v, kc, vc, part, G,
+                     Tmax, pos, theta, rot_dim, chunk, nsplit);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_attn_part<D>, dim3(Hkv, nsplit), dim3(G * 64), 0, s, kc, vc, qr, part, G, Tmax,
-                     T, chunk, nsplit);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_attn_combine<D>, dim3(Hq), dim3(1024), 0, s, part, o, nsplit);
   return hipGetLastError();
 }
@@ -246,7 +253,7 @@ hipError_t launch_d(const float* q, const float* k, const float* v, float* kc, f
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int Tmax) {
   const int64_t a = ((int64_t)Tmax + kTK - 1) / kTK, b = (kWantSplits + Hkv - 1) / Hkv;
   const int64_t nsplit = a < b ? a : b;
-  return (size_t)((int64_t)Hq * D + (int64_t)Hq * nsplit * (D + 4)) * 4;
+  return (size_t)((int64_t)Hq * nsplit * (D + 4)) * 4;
 }
 
 hipError_t launch_attn_decode(const float* q, const float* k, const float* v, float* kc, float* vc,
