@@ -61,7 +61,7 @@ typedef enum {
   QMOE_EALIGN = -3,      /* a pointer or stride is not aligned as documented */
   QMOE_EWORKSPACE = -4,  /* workspace missing or smaller than qmoe_workspace_bytes() */
   QMOE_EHIP = -5,        /* the HIP runtime reported an error */
-  QMOE_EUNSUPPORTED = -6 /* valid request this build does not implement */
+  QMOE_EUNSUPPORTED = -6 /* a valid request the library does not implement */
 } qmoe_status;
 
 /* Byte offsets of the six tensors inside one expert block, and its size. */
