@@ -375,7 +375,9 @@ def test_layer_call_counter_wraps(q):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("E,H,I,bits,K,T", [(64, 1024, 256, 4, 4, 16), (512, 4096, 1024, 4, 4, 64),
-                                            (512, 4096, 1024, 2, 4, 8), (8, 256, 128, 4, 8, 5)])
+                                            (512, 4096, 1024, 2, 4, 8), (8, 256, 128, 4, 8, 5),
+                                            # every expert gets 40 pairs: chunks of 32 and 8
+                                            (4, 256, 128, 4, 4, 40)])
 def test_batched_parity(q, E, H, I, bits, K, T):
     say("batched", E, H, I, bits, K, T)
     D = DeviceLayer(1004 if E == 512 else 5000 + E, 0, E, H, I, bits, K)
