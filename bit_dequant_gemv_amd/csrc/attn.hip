@@ -222,6 +222,7 @@ __global__ __launch_bounds__(1024) void k_attn_combine(const float* part, float*
 
 // keys per split: about one workgroup per CU (a workgroup fills a CU's LDS), whole
 // tiles
+// (128 ranges measured 35.7 us)
 constexpr int kWantSplits = 256;  // 512 measured slower (30.2 us)
 int attn_chunk(int Hkv, int T) {
   const int64_t want = kWantSplits;
