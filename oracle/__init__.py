@@ -77,6 +77,9 @@ __all__ = [
     "moe_layer_batched",
     "rmsnorm",
     "moe_stack",
+    "gdn_step",
+    "rope",
+    "attn_decode",
     "rel_l2",
 ]
 
@@ -287,8 +290,9 @@ def expert_ffn(block: np.ndarray, x: np.ndarray, hidden: int, inter: int, bits: 
 
 
 # --------------------------------------------------------------------------
-# Combine + residual + sigmoid gate   ([PK] Metal shaders: "MoE 결합 + 잔차 연결
-# + 시그모이드 게이트", one fused kernel)
+# Combine + residual + sigmoid gate   ([PK] "손으로 작성한 Metal 컴퓨트 셰이더":
+# the combine of the weighted experts with the residual and the sigmoid gate is
+# one fused kernel there)
 # --------------------------------------------------------------------------
 
 def combine_residual_gate(y_routed: np.ndarray, w: np.ndarray, y_shared: np.ndarray,
@@ -348,7 +352,8 @@ def moe_layer_batched(get_expert, shared_block, router_bf16, shared_gate_bf16, X
 
 
 # --------------------------------------------------------------------------
-# RMSNorm   ([PK] Metal shaders: "RMS 정규화 (두 단계: 제곱합 리덕션 + 적용)")
+# RMSNorm   ([PK] "손으로 작성한 Metal 컴퓨트 셰이더": RMS normalisation in two
+# passes, a sum-of-squares reduction and then the scaling)
 # --------------------------------------------------------------------------
 
 def rmsnorm(v: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:

@@ -586,3 +586,113 @@ def test_attn_brute_force_with_explicit_softmax():
         ref = [sum(w[t] * vals[t][d] for t in range(pos + 1)) / sum(w) for d in range(D)]
         np.testing.assert_allclose(o[h], ref, rtol=1e-12)
     np.testing.assert_array_equal(K2[0, pos + 1:], K[0, pos + 1:])   # rows past pos untouched
+
+
+# --------------------------------------------------------------------------
+# The comparison helpers every parity test relies on: rel_l2 (the bar), the
+# fp32 near-tie tolerance of the top-K, and the forced-selection branch of
+# moe_layer (the reference taken when a near-tie is exempted)
+# --------------------------------------------------------------------------
+
+def test_rel_l2_hand_cases():
+    # ||(9,12) - (6,8)|| = ||(3,4)|| = 5 against ||(6,8)|| = 10
+    assert oracle.rel_l2([9.0, 12.0], [6.0, 8.0]) == 0.5
+    # the second argument is the reference: ||(3,4)|| / ||(9,12)|| = 1/3
+    assert abs(oracle.rel_l2([6.0, 8.0], [9.0, 12.0]) - 1.0 / 3.0) < 1e-16
+    # twice the reference is one reference-norm away
+    b = np.array([1.0, -2.0, 2.0])
+    assert oracle.rel_l2(2 * b, b) == 1.0
+    assert oracle.rel_l2(b, b) == 0.0
+    # zero reference: the absolute norm of a (||(3,4,0)|| = 5)
+    assert oracle.rel_l2([3.0, 4.0, 0.0], [0.0, 0.0, 0.0]) == 5.0
+    # a small error stays linear in its size: 1e-4 relative, not 1e-8
+    c = np.array([0.0, 0.0, 2.0])
+    assert abs(oracle.rel_l2(c + [0.0, 2e-4, 0.0], c) - 1e-4) < 1e-18
+    # shapes are flattened
+    assert oracle.rel_l2(np.array([[9.0], [12.0]]), np.array([6.0, 8.0])) == 0.5
+
+
+def test_topk_tolerance_closed_form():
+    """A 3-expert router of exact bf16 values over H = 4 inputs:
+    sum_h |W[e,h] x[h]| = 4, 5 and 0, sqrt(H) = 2, so tau = 4 * 2^-24 * 2 * (4, 5, 0)."""
+    Wr = _bf16([[1.0, -2.0, 0.5, 0.0], [-1.0, 1.0, 1.0, 0.25], [0.0, 0.0, 0.0, 0.0]])
+    x = np.array([1.0, 1.0, -2.0, 4.0])
+    tau = oracle.topk_tolerance(Wr, x)
+    np.testing.assert_array_equal(tau, [2.0 ** -19, 1.25 * 2.0 ** -19, 0.0])
+    # an explicit term count replaces H in the square root
+    np.testing.assert_array_equal(oracle.topk_tolerance(Wr, x, n_terms=16), 2 * tau)
+
+
+def test_topk_tolerance_bounds_real_fp32_error_and_is_tight():
+    """On config-sized random routers, tau covers the error of sequentially
+    accumulated fp32 dot products (the worst summation order a kernel could
+    take) yet stays within a small factor of the largest error seen."""
+    rng = np.random.default_rng(17)
+    H, E = 4096, 64
+    Wr = _bf16(rng.standard_normal((E, H)) * 0.02)
+    W32 = oracle.bf16_bits_to_f64(Wr).astype(np.float32)
+    x = rng.standard_normal(H).astype(np.float32)
+    exact = oracle.router_logits(Wr, x.astype(np.float64))
+    tau = oracle.topk_tolerance(Wr, x)
+    seq = np.zeros(E, np.float32)
+    for h in range(H):                       # one fp32 rounding per term, in order
+        seq = (seq + W32[:, h] * x[h]).astype(np.float32)
+    err = np.abs(seq.astype(np.float64) - exact)
+    assert np.all(err <= tau)
+    # generous (about 130x the largest error here) but not loose: within 500x
+    assert err.max() > tau.max() / 500
+
+
+def _const_layer_block(H, I, bits, down_bias_bits):
+    """All codes zero; gate bias 1, up bias 1/64, down bias given, scales 1.
+    With x = e_0: a = 1, u = 1/64, h = silu(1)/64, y = down_bias * I * silu(1)/64."""
+    return _const_expert_block(H, I, bits, (0, 0x3F80, 0x3F80), (0, 0x3F80, 0x3C80),
+                               (0, 0x3F80, down_bias_bits))
+
+
+def test_moe_layer_forced_selection_by_hand():
+    """force_idx picks the experts and their weights are the softmax of the
+    forced logits: a forced set that is not the top-K, with experts whose
+    outputs are distinct constants, checked against hand-computed values."""
+    H, I, bits, K = 64, 64, 4, 2
+    down = [0x3F00, 0x3F80, 0x3FC0, 0x4000, 0x4020, 0x4040]   # 0.5, 1, 1.5, 2, 2.5, 3
+    blocks = [_const_layer_block(H, I, bits, d) for d in down]
+    shared = _const_layer_block(H, I, bits, 0x4080)           # 4
+    logit = [0.5, -1.0, 2.0, 0.25, 1.5, -0.5]
+    Wr = np.zeros((6, H), np.float32)
+    Wr[:, 0] = logit
+    Wr = _bf16(Wr)
+    gate = np.zeros(H, np.uint16)                             # gamma = 1/2
+    x = np.zeros(H)
+    x[0] = 1.0
+    r = np.linspace(-1.0, 1.0, H)
+    s1 = 1.0 / (1.0 + math.exp(-1.0))                        # silu(1)
+    y = [d * I * s1 / 64 for d in (0.5, 1.0, 1.5, 2.0, 2.5, 3.0)]
+    y_sh = 4.0 * I * s1 / 64
+
+    # natural selection: experts 2 and 4 (logits 2 and 1.5)
+    out_nat, d = oracle.moe_layer(lambda e: blocks[e], shared, Wr, gate, x, r, H, I, bits, K,
+                                  return_details=True)
+    assert list(d["idx"]) == [2, 4]
+    w_nat = [1.0 / (1.0 + math.exp(-0.5)), 1.0 / (1.0 + math.exp(0.5))]
+    np.testing.assert_allclose(d["w"], w_nat, rtol=1e-15)
+    np.testing.assert_allclose(out_nat, r + w_nat[0] * y[2] + w_nat[1] * y[4] + 0.5 * y_sh,
+                               rtol=1e-13, atol=1e-15)
+    # forcing the natural set changes nothing
+    out_same = oracle.moe_layer(lambda e: blocks[e], shared, Wr, gate, x, r, H, I, bits, K,
+                                force_idx=[2, 4])
+    np.testing.assert_array_equal(out_same, out_nat)
+
+    # forced {0, 3}: weights softmax(0.5, 0.25), not uniform and not the full softmax
+    out_f, d = oracle.moe_layer(lambda e: blocks[e], shared, Wr, gate, x, r, H, I, bits, K,
+                                force_idx=[0, 3], return_details=True)
+    e0, e3 = math.exp(0.5), math.exp(0.25)
+    w_f = [e0 / (e0 + e3), e3 / (e0 + e3)]
+    assert list(d["idx"]) == [0, 3]
+    np.testing.assert_allclose(d["w"], w_f, rtol=1e-15)
+    np.testing.assert_allclose(out_f, r + w_f[0] * y[0] + w_f[1] * y[3] + 0.5 * y_sh,
+                               rtol=1e-13, atol=1e-15)
+    # the forced order is kept: [3, 0] gives the same output with swapped weights
+    _, d = oracle.moe_layer(lambda e: blocks[e], shared, Wr, gate, x, r, H, I, bits, K,
+                            force_idx=[3, 0], return_details=True)
+    np.testing.assert_allclose(d["w"], w_f[::-1], rtol=1e-15)
