@@ -80,6 +80,9 @@ __all__ = [
     "gdn_step",
     "rope",
     "attn_decode",
+    "deinterleave_q",
+    "head_rmsnorm",
+    "attn_decode_qgate",
     "rel_l2",
 ]
 
@@ -458,6 +461,50 @@ def attn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, K: np.ndarray, V: n
         p = np.exp(s - s.max())
         o[h] = (p / p.sum()) @ V[g, :pos + 1]
     return o, K, V
+
+
+def deinterleave_q(qg: np.ndarray, D: int) -> tuple[np.ndarray, np.ndarray]:
+    """The query projection's output with the query and its gate interleaved by
+    head: row h of qg ([Hq][2D]) holds head h's D query values followed by its D
+    gate values.  Returns (q [Hq][D], gate [Hq][D]).
+
+    [PK] "손으로 작성한 Metal 컴퓨트 셰이더" lists RoPE fused with a
+    de-interleave of Q; the page gives no layout, and this per-head
+    [query | gate] split is the reading taken (the gate half is handed on, not
+    applied: the page does not say what uses it)."""
+    qg = np.asarray(qg, dtype=np.float64)
+    if qg.shape[-1] != 2 * D:
+        raise ValueError("qg rows must hold 2*D values")
+    return qg[..., :D].copy(), qg[..., D:].copy()
+
+
+def head_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMS normalisation of every row of x ([rows][D]) over its D values:
+    x / sqrt(mean(x^2) + eps) * w, with one weight vector w [D] for all rows
+    ([PK] "손으로 작성한 Metal 컴퓨트 셰이더": the K normalisation fused with
+    RoPE; the weight form is read as a plain multiply, as for the layer's RMSNorm)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64).reshape(-1)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
+def attn_decode_qgate(qg: np.ndarray, k: np.ndarray, v: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      pos: int, theta: float, rot_dim: int, q_norm_w=None, k_norm_w=None,
+                      eps: float = 1e-6):
+    """One decode token of grouped-query attention from the interleaved query
+    projection: q and gate de-interleaved from qg, q and k RMS-normalised per head
+    when a weight is given (None: no normalisation), then ``attn_decode`` (RoPE,
+    cache append, attention).  Returns (o [Hq][D], gate [Hq][D], K', V')."""
+    D = np.asarray(k).shape[-1]
+    q, gate = deinterleave_q(qg, D)
+    if q_norm_w is not None:
+        q = head_rmsnorm(q, q_norm_w, eps)
+    k = np.asarray(k, dtype=np.float64)
+    if k_norm_w is not None:
+        k = head_rmsnorm(k, k_norm_w, eps)
+    o, K2, V2 = attn_decode(q, k, v, K, V, pos, theta, rot_dim)
+    return o, gate, K2, V2
 
 
 # --------------------------------------------------------------------------

@@ -696,3 +696,65 @@ def test_moe_layer_forced_selection_by_hand():
     _, d = oracle.moe_layer(lambda e: blocks[e], shared, Wr, gate, x, r, H, I, bits, K,
                             force_idx=[3, 0], return_details=True)
     np.testing.assert_allclose(d["w"], w_f[::-1], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# The attention step's input side: Q de-interleave and the per-head RMS norm
+# --------------------------------------------------------------------------
+
+def test_deinterleave_q_hand_case():
+    qg = np.array([[1.0, 2.0, 3.0, 4.0], [5.0, 6.0, 7.0, 8.0]])
+    q, gate = oracle.deinterleave_q(qg, 2)
+    np.testing.assert_array_equal(q, [[1.0, 2.0], [5.0, 6.0]])
+    np.testing.assert_array_equal(gate, [[3.0, 4.0], [7.0, 8.0]])
+    with pytest.raises(ValueError):
+        oracle.deinterleave_q(qg, 3)
+
+
+def test_head_rmsnorm_hand_cases():
+    # row (3, 4): mean square 12.5; row (-2, -2, -2, -2) is constant
+    x = np.array([[3.0, 4.0]])
+    np.testing.assert_allclose(oracle.head_rmsnorm(x, [1.0, 2.0], 0.0),
+                               [[3.0 / math.sqrt(12.5), 8.0 / math.sqrt(12.5)]], rtol=1e-15)
+    c = np.full((1, 4), -2.0)
+    np.testing.assert_allclose(oracle.head_rmsnorm(c, np.ones(4), 1e-6), -2.0 / math.sqrt(4.0 + 1e-6),
+                               rtol=1e-15)
+    # per row, not over the whole array: scaling one row leaves the others
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((3, 8))
+    w = rng.uniform(0.9, 1.1, 8)
+    Y = oracle.head_rmsnorm(X, w, 1e-12)
+    X2 = X.copy()
+    X2[1] *= 1000.0
+    Y2 = oracle.head_rmsnorm(X2, w, 1e-12)
+    np.testing.assert_allclose(Y2, Y, rtol=1e-9)         # scale invariance, row by row
+    np.testing.assert_allclose(np.sqrt(np.mean((Y / w) ** 2, axis=1)), 1.0, rtol=1e-9)
+
+
+def test_attn_qgate_reduces_to_plain_attention():
+    """With no weights the de-interleaved query goes straight to attn_decode; with a
+    key norm the output does not change when the key is scaled (only its direction
+    enters), and at position 0 the only key's value is returned whatever the norms."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, T, pos = 4, 2, 8, 6, 4
+    qg = rng.standard_normal((Hq, 2 * D))
+    k = rng.standard_normal((Hkv, D))
+    v = rng.standard_normal((Hkv, D))
+    K = rng.standard_normal((Hkv, T, D))
+    V = rng.standard_normal((Hkv, T, D))
+    o, gate, K2, V2 = oracle.attn_decode_qgate(qg, k, v, K, V, pos, 1e4, 4)
+    o_ref, K_ref, _ = oracle.attn_decode(qg[:, :D], k, v, K, V, pos, 1e4, 4)
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(gate, qg[:, D:])
+    np.testing.assert_array_equal(K2, K_ref)
+    wk = rng.uniform(0.5, 1.5, D)
+    wq = rng.uniform(0.5, 1.5, D)
+    a = oracle.attn_decode_qgate(qg, k, v, K, V, pos, 1e4, 4, wq, wk, 0.0)
+    b = oracle.attn_decode_qgate(qg * 3.0, k * 7.0, v, K, V, pos, 1e4, 4, wq, wk, 0.0)
+    np.testing.assert_allclose(b[0], a[0], rtol=1e-12)
+    np.testing.assert_allclose(b[2][:, pos], a[2][:, pos], rtol=1e-12)
+    # the appended key is the normalised one: its rms over the unrotated dims is |w|
+    kn = oracle.head_rmsnorm(k, wk, 0.0)
+    np.testing.assert_allclose(a[2][:, pos, 4:], kn[:, 4:], rtol=1e-13)
+    o0, _, _, _ = oracle.attn_decode_qgate(qg, k, v, K, V, 0, 1e4, 8, wq, wk, 1e-6)
+    np.testing.assert_allclose(o0, np.repeat(v, Hq // Hkv, axis=0), rtol=1e-13)
