@@ -67,6 +67,7 @@ _SIGS = {
     "moe_combine_residual_gate": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp], ctypes.c_int),
     "moe_layer_forward": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
+    "moe_layer_forward_noalloc": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_layer_forward_norm": ([ctypes.POINTER(LayerC), _vp, _vp, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
                                ctypes.c_int),
     "moe_layer_forward_batched": ([ctypes.POINTER(LayerC), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
@@ -257,6 +258,22 @@ def moe_layer_forward(layer: Layer, x, residual=None, out=None, idx=None, w=None
                                   _ptr(residual, torch.float32, "residual"), _ptr(out, torch.float32, "out"),
                                   _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
                                   _ptr(ws, None, "ws"), ws.numel(), _stream()), "moe_layer_forward")
+    return out, idx, w
+
+
+def moe_layer_forward_noalloc(layer: Layer, x, residual=None, out=None, idx=None, w=None):
+    """moe_layer_forward with the library's own device scratch (no workspace, no
+    allocation inside the call when out/idx/w are given): returns (out, idx, w)."""
+    residual = residual if residual is not None else x
+    dev = x.device
+    out = out if out is not None else torch.empty_like(x)
+    idx = idx if idx is not None else torch.empty(layer.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(layer.top_k, dtype=torch.float32, device=dev)
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(layer.c()), _ptr(x, torch.float32, "x"),
+                                          _ptr(residual, torch.float32, "residual"),
+                                          _ptr(out, torch.float32, "out"), _ptr(idx, torch.int32, "idx"),
+                                          _ptr(w, torch.float32, "w"), _stream()),
+           "moe_layer_forward_noalloc")
     return out, idx, w
 
 

@@ -9,6 +9,9 @@
 
 #include "qmoe_internal.h"
 
+static_assert(QMOE_NOALLOC_SCRATCH_BYTES == qmoe::kNoAllocScratchBytes,
+              "the header states the allocation-free entry point's scratch size");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -226,6 +229,24 @@ int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual
   return hip_status(qmoe::launch_layer(*L, x, nullptr, 0.f, residual, out, topk_idx, topk_w, ws,
                                        static_cast<hipStream_t>(stream)),
                     "moe_layer_forward launch");
+}
+
+int moe_layer_forward_noalloc(const qmoe_layer* L, const float* x, const float* residual,
+                              float* out, int32_t* topk_idx, float* topk_w, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!residual || !out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  if (out == x) return fail(QMOE_EINVAL, "out must not alias x");
+  const size_t need = qmoe_workspace_bytes(L, 1);
+  if (need > qmoe::kNoAllocScratchBytes)
+    return fail(QMOE_EWORKSPACE,
+                "this layer needs %zu bytes of scratch; the allocation-free entry point has %zu "
+                "(use moe_layer_forward with a workspace)",
+                need, qmoe::kNoAllocScratchBytes);
+  return hip_status(qmoe::launch_layer_noalloc(*L, x, residual, out, topk_idx, topk_w,
+                                               static_cast<hipStream_t>(stream)),
+                    "moe_layer_forward_noalloc launch");
 }
 
 int moe_layer_forward_norm(const qmoe_layer* L, const float* h, const float* norm_w, float eps,

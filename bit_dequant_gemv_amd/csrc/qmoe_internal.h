@@ -44,6 +44,13 @@ hipError_t launch_layer(const qmoe_layer& L, const float* x, const float* norm_w
                         const float* residual, float* out, int32_t* idx, float* w, void* ws,
                         hipStream_t s);
 
+// the fused layer with its workspace in a device-global array of
+// kNoAllocScratchBytes per GPU instead of a caller's buffer (noalloc.hip); the
+// layer's workspace size must not exceed it
+constexpr size_t kNoAllocScratchBytes = (size_t)1 << 20;
+hipError_t launch_layer_noalloc(const qmoe_layer& L, const float* x, const float* residual,
+                                float* out, int32_t* idx, float* w, hipStream_t s);
+
 // a decoder stack of n layers of one shape, h <- h + MoE_l(rmsnorm(h, norm_w[l])):
 // one fused launch per layer, or (persistent) one launch per 32 layers (layer.hip)
 size_t stack_workspace_bytes(const qmoe_layer& L, int n_layers);

@@ -20,7 +20,8 @@
  *     pointers read during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *     is enqueued asynchronously; no call synchronises the device, allocates or
- *     frees memory.  Scratch memory is a caller-provided workspace.
+ *     frees memory.  Scratch memory is a caller-provided workspace (except for
+ *     moe_layer_forward_noalloc, whose scratch is a library-held device array).
  *   - Arguments are validated on the host before anything is enqueued; a
  *     negative qmoe_status is returned and nothing is launched.  A launch
  *     failure returns QMOE_EHIP.  Device faults surface at the caller's next
@@ -161,6 +162,24 @@ int moe_combine_residual_gate(const float* y_routed, const float* topk_w, const 
  */
 int moe_layer_forward(const qmoe_layer* L, const float* x, const float* residual, float* out,
                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward for callers that cannot allocate memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and result as moe_layer_forward without ws/ws_bytes:
+ * the workspace is a device-global array of QMOE_NOALLOC_SCRATCH_BYTES (1 MiB) per
+ * GPU, held by the library until the process ends.  Nothing is allocated or
+ * freed by the call.  The first call on a device looks the array up (and, unless
+ * the stream is being captured, enqueues a fill of zeros before the layer).
+ * Errors: as moe_layer_forward; QMOE_EWORKSPACE if the layer's workspace
+ * (qmoe_workspace_bytes(L, 1)) exceeds QMOE_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * state (a call counter and values tagged with it): calls on one GPU must be
+ * ordered (one stream, or event dependencies); calls that overlap race.
+ */
+#define QMOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+int moe_layer_forward_noalloc(const qmoe_layer* L, const float* x, const float* residual,
+                              float* out, int32_t* topk_idx, float* topk_w, void* stream);
 
 /*
  * The same layer with its input RMS-normalised inside the launch: a decoder
