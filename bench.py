@@ -226,6 +226,7 @@ def run_layer_bench(args, torch, q, synth, bits):
         tail = capture_graphs(torch, calls[:steps % per_graph], per_graph)[0]
     warm = (max(0, args.warmup) + per_graph - 1) // per_graph
     dt = time_graphs(torch, graphs, steps // per_graph, warm, tail)
+    spread = launch_spread(torch, graphs, per_graph)
     status = int(W.ws[4:8].view(torch.int32).item())
     if status != 0:
         raise RuntimeError(f"fused layer kernel reported status {status}")
@@ -236,9 +237,19 @@ def run_layer_bench(args, torch, q, synth, bits):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profiles(f"k_layer_w{bits}")}
+    eb = (K + 1) * expert_bytes(bits)
     extra = {"kernel": "k_layer (fused router+top-K+experts+combine, one launch per token)",
              "bytes_per_launch": lb, "avg_launch_us": round(launch_s * 1e6, 3),
-             "expert_bytes_per_launch": (K + 1) * expert_bytes(bits)}
+             "launch_spread": spread,
+             "expert_bytes_per_launch": eb,
+             # the expert GEMVs' weight bytes over the fused launch that reads them
+             "expert_gemv_GBps_in_layer": round(eb / launch_s / 1e9, 1)}
+    if bits == 4:
+        gbps5, us5 = run_expert_ffn5(torch, q, synth, W.routed, seed + 77)
+        extra["expert_ffn_swiglu_5experts_GBps"] = round(gbps5, 1)
+        extra["expert_ffn_swiglu_5experts_avg_call_us"] = round(us5, 3)
+    del W, X, graphs
+    torch.cuda.empty_cache()
     return tok_s, steps, dt, roof, extra, (seed, bits)
 
 
@@ -264,6 +275,72 @@ def run_qgemv_stream(torch, q, synth):
     launches = 16 * reps
     del codes, sb
     return per * launches / dt / 1e9, dt / launches * 1e6
+
+
+def run_stream_calibration(torch, q, sizes):
+    """Attainable read bandwidth of ONE launch as a function of its bytes: the
+    read-only streaming kernel (qmoe_stream_read) over a ring of distinct regions
+    of an 8 GiB buffer, so no launch finds its bytes in a cache.  Returns
+    {bytes: GB/s}."""
+    total = 8 << 30
+    buf = torch.empty(total // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(0x5A5A5A5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for nb in sizes:
+        nb = (nb + 255) // 256 * 256
+        n_reg = max(2, min(64, total // nb))
+        step = (total - nb) // (n_reg - 1) // 256 * 256
+        views = [buf[(i * step) // 4:(i * step + nb) // 4] for i in range(n_reg)]
+        calls = [(lambda v=v: q.qmoe_stream_read(v, nb, sink=sink)) for v in views]
+        graphs = capture_graphs(torch, calls, n_reg)
+        warm_for(torch, lambda: graphs[0].replay(), 0.1)
+        reps = max(4, int(8e9 // (nb * n_reg)))
+        dt = time_graphs(torch, graphs, reps, 1)
+        out[nb] = nb * n_reg * reps / dt / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def launch_spread(torch, graphs, launches_per_graph, repeats=25):
+    """Average launch time of each of `repeats` graph replays (launches_per_graph
+    launches each), as median, p10 and p90 in microseconds."""
+    import statistics
+    per = []
+    st = torch.cuda.current_stream()
+    for r in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        graphs[r % len(graphs)].replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / launches_per_graph)
+    per.sort()
+    q10 = per[max(0, int(0.1 * (len(per) - 1)))]
+    q90 = per[min(len(per) - 1, int(round(0.9 * (len(per) - 1))))]
+    return {"repeats": repeats, "launches_each": launches_per_graph,
+            "median_us": round(statistics.median(per), 3), "p10_us": round(q10, 3),
+            "p90_us": round(q90, 3)}
+
+
+def run_expert_ffn5(torch, q, synth, pool, seed):
+    """The expert-GEMV work of one layer as a stand-alone call: expert_ffn_swiglu
+    over 5 experts of the resident pool per call (indices drawn per call, a ring of
+    256 sets), 5 x 7,077,888 B of weights.  Returns (GB/s, average call in us)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    n_ring = 256
+    idx = torch.from_numpy(np.stack([rng.choice(pool.num_experts, 5, replace=False)
+                                     for _ in range(n_ring)]).astype(np.int32)).cuda()
+    X = make_x_ring(torch, synth, seed, 64)
+    Y = torch.empty(5, H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, q.qmoe_ffn_workspace_bytes(pool, 5)), dtype=torch.uint8, device="cuda")
+    calls = [(lambda t=t: q.expert_ffn_swiglu(pool, idx[t], X[t % 64], Y, ws)) for t in range(n_ring)]
+    dt = timed_steps(torch, calls, 4 * n_ring, n_ring, n_ring)
+    per = 5 * expert_bytes(4) + H * 4 + 5 * H * 4
+    return per * 4 * n_ring / dt / 1e9, dt / (4 * n_ring) * 1e6
 
 
 def run_copy(torch):
@@ -571,6 +648,42 @@ def run_batched_bench(args, torch, q, synth):
             "cfg": {"batch": T}}
 
 
+def device_info():
+    """GPU name (gfx target) and clocks from rocminfo, read before this process
+    initialises the GPU; empty fields if the tool is not there."""
+    import re
+    import subprocess
+    info = {}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except Exception:
+        return info
+    for block in txt.split("*******"):
+        m = re.search(r"Name:\s+(gfx\w+)", block)
+        if not m:
+            continue
+        info["gfx"] = m.group(1)
+        mk = re.search(r"Marketing Name:[ \t]*(\S[^\n]*)", block)
+        if mk:
+            info["marketing_name"] = mk.group(1).strip()
+        mc = re.search(r"Max Clock Freq\. \(MHz\):[ \t]*(\d+)", block)
+        if mc:
+            info["max_sclk_MHz"] = int(mc.group(1))
+        cu = re.search(r"Compute Unit:[ \t]*(\d+)", block)
+        if cu:
+            info["compute_units"] = int(cu.group(1))
+        break
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        for key in ("sclk", "mclk", "fclk"):
+            m = re.search(key + r" clock level: \d+: \((\d+)Mhz\)", txt)
+            if m:
+                info[key + "_MHz_now"] = int(m.group(1))
+    except Exception:
+        pass
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -588,6 +701,7 @@ def main():
               "sharding of this path is a design note, not a measured configuration.", file=sys.stderr)
         sys.exit(2)
 
+    dev_info = device_info()
     import torch
     import bit_dequant_gemv_amd as q
     import synth
@@ -602,10 +716,23 @@ def main():
         extra0["copy_1GiB_GBps"] = round(run_copy(torch), 1)
         torch.cuda.empty_cache()
         bits = 4 if args.config == 1 else 2
+        lb = layer_bytes(bits)
+        stream = run_stream_calibration(torch, q, [4 << 20, lb, 40 << 20, 400 << 20, 4 << 30])
+        extra0["stream_read_GBps_by_bytes_per_launch"] = {str(k): round(v, 1) for k, v in stream.items()}
         tok_s, steps, dt, roof, extra, (seed, _) = run_layer_bench(args, torch, q, synth, bits)
+        att = stream[(lb + 255) // 256 * 256]
+        extra0["attainable_GBps_same_bytes_per_launch"] = round(att, 1)
+        extra0["frac_of_attainable_same_bytes"] = round(roof["achieved"] / att, 4)
         cpu = None
         if not args.no_cpu_baseline:
             cpu = cpu_oracle_layer(seed, 0, bits, list(range(64)), args.cpu_seconds)
+            try:
+                from threadpoolctl import threadpool_limits
+                with threadpool_limits(limits=1):
+                    one = cpu_oracle_layer(seed, 0, bits, list(range(8)), min(10.0, args.cpu_seconds))
+                extra0["cpu_oracle_1thread_tokens_per_s"] = round(one["value"], 3)
+            except ImportError:
+                pass
         r = {"value": tok_s, "unit": "tokens/s", "steps": steps, "dt": dt, "roof": roof, "extra": extra,
              "cpu": cpu, "workload": f"moe_layer_batch1_{bits}bit", "bits": bits, "cfg": {}}
     elif args.config == 0:
@@ -622,7 +749,9 @@ def main():
     config = r.get("config") or {"workload": r["workload"], "experts": E, "hidden": H, "inter": I,
                                  "top_k": K, "shared_experts": 1, "group": 64, "bits": r["bits"]}
     config.update(r.get("cfg", {}))
-    config["device"] = torch.cuda.get_device_name(0)
+    config["device"] = dev_info.get("marketing_name") or torch.cuda.get_device_name(0)
+    config["gfx"] = dev_info.get("gfx") or getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)
+    r["extra"]["device_info"] = dev_info
     line = {
         "metric": r.get("metric", METRIC), "value": round(r["value"], 1), "unit": r["unit"], "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["dt"] * 1e3 / r["steps"], 6),

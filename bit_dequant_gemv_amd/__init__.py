@@ -76,6 +76,7 @@ _SIGS = {
     "moe_stack_forward": ([ctypes.POINTER(LayerC), ctypes.POINTER(_vp), _i32, _f32, _vp, _vp, _vp, _vp,
                            _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
     "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
+    "qmoe_stream_read": ([_vp, ctypes.c_int64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
     "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
     "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp], ctypes.c_int),
     "attn_decode_step": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz,
@@ -402,6 +403,18 @@ def attn_decode_step(q, k, v, k_cache, v_cache, pos, theta=1e7, rot_dim=None, o=
                                  rot_dim, _ptr(o, torch.float32, "o"), _ptr(ws, None, "ws"), ws.numel(),
                                  _stream()), "attn_decode_step")
     return o
+
+
+def qmoe_stream_read(buf, nbytes=None, key=0xA5A5A5A5, sink=None):
+    """One read-only streaming launch over nbytes of buf (default: all of it);
+    returns the sink tensor (written only if the xor of the data equals key)."""
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    sink = sink if sink is not None else torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(_lib.qmoe_stream_read(_ptr(buf, None, "buf"), nbytes, key, _ptr(sink, None, "sink"), _stream()),
+           "qmoe_stream_read")
+    return sink
 
 
 def rmsnorm_f32(v, weight, eps=1e-6, out=None):

@@ -377,6 +377,15 @@ int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out
                     "rmsnorm launch");
 }
 
+int qmoe_stream_read(const void* buf, int64_t bytes, uint32_t key, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(QMOE_EINVAL, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return QMOE_OK;
+  if (!buf || !aligned(buf, 16)) return fail(QMOE_EALIGN, "buf must be 16-byte aligned");
+  if (!sink || !aligned(sink, 4)) return fail(QMOE_EALIGN, "sink must be 4-byte aligned");
+  return hip_status(qmoe::launch_stream_read(buf, bytes, key, sink, static_cast<hipStream_t>(stream)),
+                    "qmoe_stream_read launch");
+}
+
 const char* qmoe_strerror(int status) {
   switch (status) {
     case QMOE_OK: return "ok";

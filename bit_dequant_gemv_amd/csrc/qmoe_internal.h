@@ -74,6 +74,10 @@ hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float
                                 float* out, int T, int32_t* idx, float* w, void* ws,
                                 hipStream_t s);
 
+// streaming-read calibration (stream.hip): reads bytes/16 16-byte words of buf
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t key, uint32_t* sink,
+                              hipStream_t s);
+
 // compute units of the current device (cached per device); 0 if it cannot be read
 int device_cus();
 

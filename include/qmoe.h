@@ -298,6 +298,18 @@ size_t qmoe_attn_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t Tma
  */
 int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out, void* stream);
 
+/*
+ * Streaming-read calibration: one launch that reads `bytes` of buf with 16-byte
+ * non-temporal loads and computes nothing, to measure the HBM bandwidth a
+ * single launch can reach for a given number of bytes (the weight streams of
+ * the layer kernels are read once per call, so their attainable rate depends on
+ * the bytes per launch).  The xor of everything read is stored to sink[0] only
+ * if it equals `key` (it keeps the loads alive; pass any value).
+ *   buf: device, 16-byte aligned; bytes: a multiple of 16 (0: nothing is done);
+ *   sink: device uint32 [1].
+ */
+int qmoe_stream_read(const void* buf, int64_t bytes, uint32_t key, uint32_t* sink, void* stream);
+
 /* Static text for a status code; thread-local detail of the last failure. */
 const char* qmoe_strerror(int status);
 const char* qmoe_last_error(void);
