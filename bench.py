@@ -160,6 +160,8 @@ def time_graphs(torch, graphs, n_replays, warmup_replays, tail=None):
     replays, recorded on the stream the graphs run on."""
     for i in range(warmup_replays):
         graphs[i % len(graphs)].replay()
+    if tail is not None:  # a graph's first replay carries one-time costs: not in the timed region
+        tail.replay()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
