@@ -77,6 +77,8 @@ _SIGS = {
                            _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
     "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
     "qmoe_stream_read": ([_vp, ctypes.c_int64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
+    "attn_decode_step_qgate": ([_vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "rmsnorm_f32": ([_vp, _vp, _f32, _i32, _vp, _vp], ctypes.c_int),
     "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp], ctypes.c_int),
     "attn_decode_step": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz,
@@ -403,6 +405,35 @@ def attn_decode_step(q, k, v, k_cache, v_cache, pos, theta=1e7, rot_dim=None, o=
                                  rot_dim, _ptr(o, torch.float32, "o"), _ptr(ws, None, "ws"), ws.numel(),
                                  _stream()), "attn_decode_step")
     return o
+
+
+def attn_decode_step_qgate(qg, k, v, k_cache, v_cache, pos, theta=1e7, rot_dim=None, q_norm_w=None,
+                           k_norm_w=None, eps=1e-6, o=None, gate=None, ws=None):
+    """attn_decode_step from the interleaved query projection qg [Hq][2D] (per head:
+    D query values, then D gate values), with optional per-head RMS normalisation
+    of q and k.  Returns (o [Hq][D], gate [Hq][D])."""
+    Hq, D2x = qg.shape
+    Hkv, Tmax, D = k_cache.shape
+    rot_dim = D if rot_dim is None else rot_dim
+    if D2x != 2 * D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(k.shape) != (Hkv, D) \
+            or tuple(v.shape) != (Hkv, D):
+        raise ValueError("qg [Hq][2D], k and v [Hkv][D], caches [Hkv][Tmax][D]")
+    for wgt in (q_norm_w, k_norm_w):
+        if wgt is not None and tuple(wgt.shape) != (D,):
+            raise ValueError("norm weights are [D]")
+    o = o if o is not None else torch.empty(Hq, D, dtype=torch.float32, device=qg.device)
+    gate = gate if gate is not None else torch.empty(Hq, D, dtype=torch.float32, device=qg.device)
+    if ws is None:
+        ws = torch.empty(max(256, qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax)), dtype=torch.uint8,
+                         device=qg.device)
+    _check(_lib.attn_decode_step_qgate(
+        _ptr(qg, torch.float32, "qg"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+        _ptr(q_norm_w, torch.float32, "q_norm_w") if q_norm_w is not None else None,
+        _ptr(k_norm_w, torch.float32, "k_norm_w") if k_norm_w is not None else None, eps,
+        _ptr(k_cache, torch.float32, "k_cache"), _ptr(v_cache, torch.float32, "v_cache"), Hq, Hkv, D, Tmax,
+        pos, theta, rot_dim, _ptr(o, torch.float32, "o"), _ptr(gate, torch.float32, "gate"),
+        _ptr(ws, None, "ws"), ws.numel(), _stream()), "attn_decode_step_qgate")
+    return o, gate
 
 
 def qmoe_stream_read(buf, nbytes=None, key=0xA5A5A5A5, sink=None):

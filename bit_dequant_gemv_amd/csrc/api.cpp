@@ -368,6 +368,31 @@ int attn_decode_step(const float* q, const float* k, const float* v, float* k_ca
                     "attn_decode_step launch");
 }
 
+int attn_decode_step_qgate(const float* qg, const float* k, const float* v, const float* q_norm_w,
+                           const float* k_norm_w, float eps, float* k_cache, float* v_cache, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t Tmax, int32_t pos, float theta, int32_t rot_dim,
+                           float* o, float* gate, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn_shape(Hq, Hkv, D, Tmax);
+  if (rc) return rc;
+  if (pos < 0 || pos >= Tmax) return fail(QMOE_ESHAPE, "pos must be in [0, Tmax)");
+  if (rot_dim < 0 || rot_dim > D || rot_dim % 2) return fail(QMOE_ESHAPE, "rot_dim must be even, 0..D");
+  if (!(theta > 0.0f)) return fail(QMOE_EINVAL, "theta must be > 0");
+  if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");
+  if ((rc = check_vec(qg, "qg")) || (rc = check_vec(k, "k")) || (rc = check_vec(v, "v")) ||
+      (rc = check_vec(k_cache, "k_cache")) || (rc = check_vec(v_cache, "v_cache")) ||
+      (rc = check_vec(o, "o")))
+    return rc;
+  if ((q_norm_w && !aligned(q_norm_w, 4)) || (k_norm_w && !aligned(k_norm_w, 4)) || (gate && !aligned(gate, 4)))
+    return fail(QMOE_EALIGN, "q_norm_w, k_norm_w and gate must be 4-byte aligned");
+  const size_t need = qmoe_attn_workspace_bytes(Hq, Hkv, D, Tmax);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  return hip_status(qmoe::launch_attn_decode(qg, k, v, k_cache, v_cache, Hq, Hkv, D, Tmax, pos, theta,
+                                             rot_dim, o, ws, static_cast<hipStream_t>(stream), true,
+                                             q_norm_w, k_norm_w, eps, gate),
+                    "attn_decode_step_qgate launch");
+}
+
 int rmsnorm_f32(const float* v, const float* w, float eps, int32_t n, float* out, void* stream) {
   if (n < 0) return fail(QMOE_EINVAL, "n must be >= 0");
   if (!(eps >= 0.0f)) return fail(QMOE_EINVAL, "eps must be >= 0");

@@ -41,17 +41,31 @@ constexpr int rec() {
 // its group's q rows into LDS; the workgroup whose range holds pos rotates the new
 // k, writes k and v to row pos of the caches and puts them into its tile directly
 // (no other workgroup reads that row in this call).
+// The query side: q rows of q_stride floats (D, or 2D when the query projection
+// interleaves each head's D query values with its D gate values: the query is the
+// first half of the row); qnw / knw: RMS-normalisation weights [D] of q and k, or
+// null; gate: the rows' second halves copied out ([Hq][D]), or null.
+struct AttnQ {
+  int q_stride;
+  const float* qnw;
+  const float* knw;
+  float eps;
+  float* gate;
+};
+
 template <int D>
 __global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float* knew,
                                                     const float* vnew, float* kc, float* vc,
                                                     float* part, int G, int64_t Tmax, int pos,
-                                                    float theta, int rot_dim, int chunk, int nsplit) {
+                                                    float theta, int rot_dim, int chunk, int nsplit,
+                                                    AttnQ Q) {
   constexpr int KS = D + 4;  // padded K row in LDS: lanes reading different rows spread over banks
   __shared__ __align__(16) float s_k[kTK * KS];
   __shared__ __align__(16) float s_v[kTK * D];
   __shared__ __align__(16) float s_q[16 * D];
   __shared__ float s_cs[2][D / 2];                // cos, sin of the rotation pairs
   __shared__ __align__(16) float s_kn[D], s_vn[D];  // the token's rotated k and its v
+  __shared__ float s_qr[16], s_kr;                 // RMS scales of the q heads and of k
   const int g = blockIdx.x, split = blockIdx.y;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = g * G + wv;
@@ -70,18 +84,42 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float*
     s_cs[0][i] = (float)cs;
     s_cs[1][i] = (float)sn;
   }
+  // RMS normalisation scales, 1 / sqrt(mean(x^2) + eps): wave wv for query head
+  // h = g*G + wv, wave 0 of the workgroup that owns pos for the new key
+  auto rms_scale = [&](const float* x) -> float {
+    float ss = 0.f;
+#pragma unroll
+    for (int d = lane; d < D; d += 64) ss = fmaf(x[d], x[d], ss);
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) ss += __shfl_xor(ss, o2);
+    return 1.0f / sqrtf(ss / (float)D + Q.eps);
+  };
+  if (Q.qnw) {
+    const float r = rms_scale(q + (int64_t)h * Q.q_stride);
+    if (lane == 0) s_qr[wv] = r;
+  }
+  if (Q.knw && owns_pos && wv == 0) {
+    const float r = rms_scale(knew + (int64_t)g * D);
+    if (lane == 0) s_kr = r;
+  }
+  if (Q.gate && split == 0)  // the gate halves of the group's query rows, copied out
+    for (int i = threadIdx.x; i < G * D; i += nthr)
+      Q.gate[(int64_t)(g * G + i / D) * D + i % D] = q[(int64_t)(g * G + i / D) * Q.q_stride + D + i % D];
   __syncthreads();
-  // x_d of a row rotated: pair (d, d + half) for d < half, (d - half, d) below rot_dim
-  auto rot = [&](const float* x, int d) -> float {
-    if (d < half) return x[d] * s_cs[0][d] - x[d + half] * s_cs[1][d];
-    if (d < rot_dim) return x[d] * s_cs[0][d - half] + x[d - half] * s_cs[1][d - half];
-    return x[d];
+  // x_d of a row, scaled by r * w_d (normalised) when w is given, then rotated:
+  // pair (d, d + half) for d < half, (d - half, d) below rot_dim
+  auto rot = [&](const float* x, int d, float r, const float* w) -> float {
+    auto val = [&](int e) { return w ? x[e] * r * w[e] : x[e]; };
+    if (d < half) return val(d) * s_cs[0][d] - val(d + half) * s_cs[1][d];
+    if (d < rot_dim) return val(d) * s_cs[0][d - half] + val(d - half) * s_cs[1][d - half];
+    return val(d);
   };
   for (int i = threadIdx.x; i < G * D; i += nthr)
-    s_q[i] = rot(q + (int64_t)(g * G + i / D) * D, i % D);
+    s_q[i] = rot(q + (int64_t)(g * G + i / D) * Q.q_stride, i % D, Q.qnw ? s_qr[i / D] : 1.f, Q.qnw);
   if (owns_pos) {
     for (int d = threadIdx.x; d < D; d += nthr) {
-      const float kr = rot(knew + (int64_t)g * D, d), vr = vnew[(int64_t)g * D + d];
+      const float kr = rot(knew + (int64_t)g * D, d, Q.knw ? s_kr : 1.f, Q.knw),
+                  vr = vnew[(int64_t)g * D + d];
       s_kn[d] = kr;
       s_vn[d] = vr;
       kg[(int64_t)pos * D + d] = kr;
@@ -234,13 +272,13 @@ int attn_chunk(int Hkv, int T) {
 template <int D>
 hipError_t launch_d(const float* q, const float* k, const float* v, float* kc, float* vc, int Hq,
                     int Hkv, int64_t Tmax, int pos, float theta, int rot_dim, float* o, float* ws,
-                    hipStream_t s) {
+                    const AttnQ& Q, hipStream_t s) {
   const int T = pos + 1, G = Hq / Hkv;
   const int chunk = attn_chunk(Hkv, T);
   const int nsplit = (T + chunk - 1) / chunk;
   float* part = ws;
   hipLaunchKernelGGL(k_attn_part<D>, dim3(Hkv, nsplit), dim3(G * 64), 0, s, q, k, v, kc, vc, part, G,
-                     Tmax, pos, theta, rot_dim, chunk, nsplit);
+                     Tmax, pos, theta, rot_dim, chunk, nsplit, Q);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_attn_combine<D>, dim3(Hq), dim3(1024), 0, s, part, o, nsplit);
@@ -259,11 +297,18 @@ size_t attn_workspace_bytes(int Hq, int Hkv, int D, int Tmax) {
 
 hipError_t launch_attn_decode(const float* q, const float* k, const float* v, float* kc, float* vc,
                               int Hq, int Hkv, int D, int Tmax, int pos, float theta, int rot_dim,
-                              float* o, void* ws, hipStream_t s) {
+                              float* o, void* ws, hipStream_t s, bool q_gate_rows,
+                              const float* q_norm_w, const float* k_norm_w, float eps, float* gate) {
   float* w = static_cast<float*>(ws);
-  if (D == 64) return launch_d<64>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, s);
-  if (D == 128) return launch_d<128>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, s);
-  return launch_d<256>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, s);
+  AttnQ Q;
+  Q.q_stride = q_gate_rows ? 2 * D : D;
+  Q.qnw = q_norm_w;
+  Q.knw = k_norm_w;
+  Q.eps = eps;
+  Q.gate = q_gate_rows ? gate : nullptr;
+  if (D == 64) return launch_d<64>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, Q, s);
+  if (D == 128) return launch_d<128>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, Q, s);
+  return launch_d<256>(q, k, v, kc, vc, Hq, Hkv, Tmax, pos, theta, rot_dim, o, w, Q, s);
 }
 
 }  // namespace qmoe

@@ -64,9 +64,13 @@ hipError_t launch_gdn_step(float* S, const float* q, const float* k, const float
 
 // full-attention decode (attn.hip); D in {64, 128, 256}, Hq / Hkv <= 16
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int Tmax);
+// q_gate_rows: q rows hold 2D floats (query, then gate); q/k_norm_w: RMS weights or
+// null; gate: where the gate halves go (q_gate_rows only), or null
 hipError_t launch_attn_decode(const float* q, const float* k, const float* v, float* kc, float* vc,
                               int Hq, int Hkv, int D, int Tmax, int pos, float theta, int rot_dim,
-                              float* o, void* ws, hipStream_t s);
+                              float* o, void* ws, hipStream_t s, bool q_gate_rows = false,
+                              const float* q_norm_w = nullptr, const float* k_norm_w = nullptr,
+                              float eps = 0.f, float* gate = nullptr);
 
 // batched decode (batched.hip)
 size_t batched_workspace_bytes(const qmoe_layer& L, int T);

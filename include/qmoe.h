@@ -289,6 +289,25 @@ int attn_decode_step(const float* q, const float* k, const float* v, float* k_ca
                      float theta, int32_t rot_dim, float* o, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * attn_decode_step from the query projection's output, with the steps the page
+ * fuses into its RoPE kernel ([PK] "손으로 작성한 Metal 컴퓨트 셰이더": RoPE fused
+ * with the Q de-interleave and the K normalisation):
+ *   q[h], gate[h] <- qg[h][0:D], qg[h][D:2D]  (each head's row holds its D query
+ *                                               values, then its D gate values);
+ *   q[h] <- q[h] / sqrt(mean(q[h]^2) + eps) * q_norm_w   (if q_norm_w is not NULL);
+ *   k[g] <- k[g] / sqrt(mean(k[g]^2) + eps) * k_norm_w   (if k_norm_w is not NULL);
+ *   then RoPE, the cache append and the attention of attn_decode_step.
+ *   qg: device float [Hq][2D], 16-byte aligned; q_norm_w, k_norm_w: device float [D] or
+ *   NULL; gate: device float [Hq][D] (written: the de-interleaved gate halves, handed
+ *   on unapplied) or NULL; every other argument as for attn_decode_step (the same
+ *   workspace size).  eps >= 0.
+ */
+int attn_decode_step_qgate(const float* qg, const float* k, const float* v, const float* q_norm_w,
+                           const float* k_norm_w, float eps, float* k_cache, float* v_cache, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t Tmax, int32_t pos, float theta, int32_t rot_dim,
+                           float* o, float* gate, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for attn_decode_step (0 for a bad shape). */
 size_t qmoe_attn_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t Tmax);
 

@@ -49,6 +49,7 @@ K_GATE_BIAS, K_UP_BIAS, K_DOWN_BIAS = 6, 7, 8
 K_ROUTER, K_SHARED_GATE, K_X, K_NORM_W = 9, 10, 11, 12
 K_GDN_STATE, K_GDN_Q, K_GDN_K, K_GDN_V, K_GDN_ALPHA, K_GDN_BETA = 13, 14, 15, 16, 17, 18
 K_ATTN_Q, K_ATTN_K, K_ATTN_V, K_ATTN_KCACHE, K_ATTN_VCACHE = 19, 20, 21, 22, 23
+K_ATTN_QG, K_ATTN_QNW, K_ATTN_KNW = 24, 25, 26
 
 # distributions of the synthetic workload
 SCALE_LO, SCALE_HI = 0.001, 0.02     # bf16 scale ~ U(0.001, 0.02)
@@ -220,6 +221,21 @@ def attn_token(seed: int, layer: int, token: int, Hq: int, Hkv: int, D: int):
     k = normal_f32(seed, tensor_id(K_ATTN_K, t, layer), Hkv * D, 1.0).reshape(Hkv, D)
     v = normal_f32(seed, tensor_id(K_ATTN_V, t, layer), Hkv * D, 1.0).reshape(Hkv, D)
     return q, k, v
+
+
+def attn_token_qg(seed: int, layer: int, token: int, Hq: int, Hkv: int, D: int):
+    """The query projection's output qg [Hq][2D] (per head: query, then gate),
+    fp32 ~N(0, 2), and this token's k ~N(0, 1) and v ~N(0, 1) [Hkv][D]."""
+    t = token % 4096
+    qg = normal_f32(seed, tensor_id(K_ATTN_QG, t, layer), Hq * 2 * D, 2.0).reshape(Hq, 2 * D)
+    _, k, v = attn_token(seed, layer, token, 1, Hkv, D)
+    return qg, k, v
+
+
+def attn_norm_weights(seed: int, layer: int, D: int):
+    """RMS-normalisation weights of q and k, fp32 ~U(0.9, 1.1) [D] each."""
+    return (uniform_f32(seed, tensor_id(K_ATTN_QNW, 0, layer), D, NORM_LO, NORM_HI),
+            uniform_f32(seed, tensor_id(K_ATTN_KNW, 0, layer), D, NORM_LO, NORM_HI))
 
 
 def gdn_token(seed: int, layer: int, token: int, heads: int, dk: int, dv: int):

@@ -594,3 +594,44 @@ def test_attn_decode_consecutive_tokens(q):
     """Three tokens in a row: each appends its key and value and sees the earlier ones."""
     say("attention decode, 3 tokens")
     _attn_check(q, 8, 2, 128, 200, 60, 128, 1e6, tokens=3)
+
+
+QGATE_CASES = [  # (Hq, Hkv, D, Tmax, pos, rot_dim, theta, q norm, k norm)
+    (4, 2, 64, 40, 37, 64, 1e4, True, True), (16, 1, 256, 300, 299, 64, 1e7, True, True),
+    (8, 8, 128, 65, 0, 0, 1e4, False, True), (32, 2, 256, 4096, 4095, 64, 1e7, True, False),
+    (3, 1, 128, 100, 50, 128, 1e4, False, False),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,Tmax,pos,rot,theta,qn,kn", QGATE_CASES)
+def test_attn_decode_qgate_parity(q, Hq, Hkv, D, Tmax, pos, rot, theta, qn, kn):
+    """The query projection's rows de-interleaved into query and gate, q and k
+    RMS-normalised per head (when weighted), then RoPE, cache append and attention:
+    against the oracle, three tokens in a row."""
+    say("attention decode qgate", Hq, Hkv, D, Tmax, pos, rot, theta, qn, kn)
+    seed = 1007
+    K0, V0 = synth.attn_cache(seed, 0, Hkv, Tmax, D)
+    kc, vc = torch.from_numpy(K0).cuda(), torch.from_numpy(V0).cuda()
+    kc[:, pos + 1:] = float("nan")
+    vc[:, pos + 1:] = float("nan")
+    wq, wk = synth.attn_norm_weights(seed, 0, D)
+    dwq = torch.from_numpy(wq).cuda() if qn else None
+    dwk = torch.from_numpy(wk).cuda() if kn else None
+    for i in range(min(3, Tmax - pos)):
+        p = pos + i
+        Kh, Vh = kc.cpu().numpy(), vc.cpu().numpy()
+        qg, kk, vv = synth.attn_token_qg(seed, 0, p, Hq, Hkv, D)
+        o, gate = q.attn_decode_step_qgate(*(torch.from_numpy(a).cuda() for a in (qg, kk, vv)), kc, vc, p,
+                                           theta, rot, q_norm_w=dwq, k_norm_w=dwk, eps=1e-6)
+        torch.cuda.synchronize()
+        oref, gref, Kref, Vref = oracle.attn_decode_qgate(qg, kk, vv, np.nan_to_num(Kh), np.nan_to_num(Vh), p,
+                                                          theta, rot, wq if qn else None, wk if kn else None,
+                                                          1e-6)
+        r = _rel(o.cpu().numpy(), oref)
+        say("  pos", p, "o rel_l2", r)
+        assert r <= 1e-4
+        assert np.array_equal(gate.cpu().numpy(), gref.astype(np.float32))
+        K2, V2 = kc.cpu().numpy(), vc.cpu().numpy()
+        assert _rel(K2[:, p], Kref[:, p]) <= 1e-6 and np.array_equal(V2[:, p], vv)
+        assert np.array_equal(K2[:, :p], Kh[:, :p]) and np.array_equal(V2[:, :p], Vh[:, :p])
+        assert np.isnan(K2[:, p + 1:]).all() and np.isnan(V2[:, p + 1:]).all()
