@@ -650,6 +650,50 @@ def run_batched_bench(args, torch, q, synth):
             "cfg": {"batch": T}}
 
 
+PHASES = ["start", "x in LDS", "router dots done, shared rows issued", "x planes", "shared gate/up dots",
+          "logits polled", "top-K ranked", "routed rows issued", "routed gate/up done (wave 0)",
+          "all flags seen", "h in LDS", "h planes", "down rows", "end"]
+
+
+def run_phase_probe(args, torch, q, synth):
+    """Phase timeline of the fused layer from the instrumented library: thread 0 of
+    every workgroup stamps the 100 MHz real-time counter at each phase boundary.
+    Prints, per phase, the median over the last 64 calls of the p10 / median / max
+    over the workgroups, in microseconds from the earliest workgroup start."""
+    import numpy as np
+    import ctypes
+    bits = 4 if args.config == 1 else 2
+    seed = 1001 if bits == 4 else 1002
+    W = LayerWorkload(seed, 0, bits, torch, q, synth)
+    n = 256
+    X = make_x_ring(torch, synth, seed, n)
+    out = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    calls = [(lambda t=t: q.moe_layer_forward(W.L, X[t], X[t], out, idx, w, W.ws)) for t in range(n)]
+    graphs = capture_graphs(torch, calls, n)
+    dt = time_graphs(torch, graphs, 16, 16)
+    buf = np.zeros(64 * 512 * 16, dtype=np.uint32)
+    rc = q.raw_lib().qmoe_phase_probe_read(ctypes.c_void_p(buf.ctypes.data))
+    if rc != 0:
+        raise RuntimeError(f"qmoe_phase_probe_read failed ({rc})")
+    nb = H // 16
+    P = buf.reshape(64, 512, 16)[:, :nb, :len(PHASES)].astype(np.int64)
+    stats = np.zeros((64, len(PHASES), 3))
+    for c in range(64):
+        t0 = P[c, :, 0].min()
+        d = ((P[c] - t0) % (1 << 32)) * 0.01  # 100 MHz ticks -> us
+        stats[c] = np.stack([np.percentile(d, 10, axis=0), np.median(d, axis=0), d.max(axis=0)], axis=1)
+    med = np.median(stats, axis=0)
+    print(f"fused layer, {bits}-bit, E={E} H={H} I={I} K={K}: {dt / (16 * n) * 1e6:.3f} us per launch (events)")
+    print(f"{'phase':40s} {'p10':>7s} {'median':>7s} {'max':>7s}  (us from the first workgroup's start)")
+    for k, name in enumerate(PHASES):
+        print(f"{name:40s} {med[k, 0]:7.2f} {med[k, 1]:7.2f} {med[k, 2]:7.2f}")
+    print(json.dumps({"phase_probe": True, "bits": bits, "avg_launch_us": round(dt / (16 * n) * 1e6, 3),
+                      "phases_median_us": {name: round(float(med[k, 1]), 3) for k, name in enumerate(PHASES)},
+                      "phases_max_us": {name: round(float(med[k, 2]), 3) for k, name in enumerate(PHASES)}}))
+
+
 def device_info():
     """GPU name (gfx target) and clocks from rocminfo, read before this process
     initialises the GPU; empty fields if the tool is not there."""
@@ -697,7 +741,12 @@ def main():
     ap.add_argument("--persistent", action="store_true",
                     help="config 3: the persistent stack kernel (32 layers per launch) instead of "
                          "one fused launch per layer")
+    ap.add_argument("--phase-probe", action="store_true",
+                    help="configs 1/2: load the instrumented library (build.py --probe) and print the "
+                         "fused layer's phase timeline instead of the benchmark line")
     args = ap.parse_args()
+    if args.phase_probe:
+        os.environ["QMOE_LIBRARY"] = "probe"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a measured configuration.", file=sys.stderr)
@@ -708,6 +757,11 @@ def main():
     import bit_dequant_gemv_amd as q
     import synth
     torch.cuda.set_device(0)
+    if args.phase_probe:
+        if args.config not in (1, 2):
+            raise SystemExit("--phase-probe covers configs 1 and 2")
+        run_phase_probe(args, torch, q, synth)
+        return
     extra0 = {}
     if args.config in (1, 2):
         # stand-alone GEMV stream and copy reference first, on an otherwise empty device

@@ -15,7 +15,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+# QMOE_LIBRARY=probe loads the instrumented build (phase timestamps in the fused
+# layer; see build.py --probe) instead of the product library
+LIB_PATH = os.path.join(_HERE, "libqmoe_probe.so" if os.environ.get("QMOE_LIBRARY") == "probe"
+                        else "libqmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "

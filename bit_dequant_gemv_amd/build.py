@@ -35,8 +35,8 @@ def _run(cmd, verbose):
         print("\n".join(noise))
 
 
-def _library(srcs, out, extra, verbose, jobs):
-    build_dir = os.path.join(os.path.dirname(out), "_build")
+def _library(srcs, out, extra, verbose, jobs, build_subdir="_build"):
+    build_dir = os.path.join(os.path.dirname(out), build_subdir)
     os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
@@ -61,6 +61,18 @@ def build_qmoe(verbose=False, jobs=None):
                     jobs or min(8, os.cpu_count() or 4))
 
 
+def build_probe(verbose=False, jobs=None):
+    """libqmoe_probe.so: the same sources with QMOE_PHASE_PROBE defined, so the fused
+    layer records per-workgroup phase timestamps (bench.py --phase-probe reads them).
+    Not part of the product build."""
+    csrc = os.path.join(HERE, "csrc")
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip",
+                                            "attn.hip", "noalloc.hip", "stream.hip")]
+    return _library(srcs, os.path.join(HERE, "libqmoe_probe.so"),
+                    ["-I", os.path.join(ROOT, "include"), "-I", csrc, "-DQMOE_PHASE_PROBE"], verbose,
+                    jobs or min(8, os.cpu_count() or 4), build_subdir="_build_probe")
+
+
 def build_synth(verbose=False, jobs=None):
     sdir = os.path.join(ROOT, "synth")
     return _library([os.path.join(sdir, "csrc", "synth.hip")], os.path.join(sdir, "libqmoe_synth.so"),
@@ -72,5 +84,8 @@ def build_all(verbose=False):
 
 
 if __name__ == "__main__":
-    for p in build_all(verbose="-v" in sys.argv):
-        print("built", p)
+    if "--probe" in sys.argv:
+        print("built", build_probe(verbose="-v" in sys.argv))
+    else:
+        for p in build_all(verbose="-v" in sys.argv):
+            print("built", p)

@@ -54,6 +54,32 @@ namespace qmoe {
 
 namespace {
 
+// Phase timestamps (a build with QMOE_PHASE_PROBE defined only): thread 0 of every
+// workgroup records the real-time counter (100 MHz) at the phase boundaries of
+// the single-layer kernel and stores them at the end, per call number modulo 64,
+// so the recording adds no memory traffic while the layer runs.  The product
+// build compiles none of it.
+#ifdef QMOE_PHASE_PROBE
+constexpr int kProbeCalls = 64, kProbeWgs = 512, kProbePhases = 16;
+__device__ uint32_t g_phase[kProbeCalls * kProbeWgs * kProbePhases];
+#define QMOE_PT_DECL uint32_t pt_[kProbePhases] = {0}
+#define QMOE_PT(k)                                                        \
+  do {                                                                    \
+    if (!STACK && threadIdx.x == 0) pt_[k] = (uint32_t)__builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define QMOE_PT_STORE()                                                                   \
+  do {                                                                                    \
+    if (!STACK && threadIdx.x == 0 && blockIdx.x < kProbeWgs) {                          \
+      for (int k_ = 0; k_ < kProbePhases; ++k_)                                           \
+        g_phase[((s_tag % kProbeCalls) * kProbeWgs + blockIdx.x) * kProbePhases + k_] = pt_[k_]; \
+    }                                                                                     \
+  } while (0)
+#else
+#define QMOE_PT_DECL
+#define QMOE_PT(k)
+#define QMOE_PT_STORE()
+#endif
+
 constexpr int kLB = 512;         // threads per workgroup
 constexpr int kLW = kLB / 64;    // waves per workgroup
 constexpr int kRB = 16;          // output rows per workgroup
@@ -204,6 +230,7 @@ __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) 
 
 template <int BITS, int H, int I, bool STACK, class Args>
 __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
+  QMOE_PT_DECL;
   // ---- compile-time geometry
   constexpr int CH = H * BITS / 128;            // 16-byte chunks per gate/up row
   constexpr int LGH = CH >= 64 ? 64 : CH;       // lanes per gate/up row
@@ -280,6 +307,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         vector memory completes in issue order, and a straight run of loads
   //         lets each use below wait for its own data only (a conditional load
   //         makes the compiler wait for everything).
+  QMOE_PT(0);
   const uint32_t epoch = __hip_atomic_load(A.ctrl + CTRL_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int xi = min((int)tx, H / 8 - 1);
   float gx[8], nw[8];
@@ -370,6 +398,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     reinterpret_cast<float4*>(s_x)[2 * tx + 1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
   }
   __syncthreads();
+  QMOE_PT(1);
 
   // ---- 2. router dots -> logits (every wave has read the epoch itself)
   // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
@@ -417,6 +446,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // waits for (the down item in registers: HBM would otherwise idle during the
   // top-K)
   shared_fetch(Lp.sblk, qsp, ssp, dq[0], dsc[0]);
+  QMOE_PT(2);
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
   prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
@@ -426,6 +456,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   }
   if (tx < kFusedMaxK) s_pick[tx] = 0;  // no pick: key 0, expert ~0 = -1
   __syncthreads();
+  QMOE_PT(3);
   const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_tag);
 
   uint64_t* hs = Lp.hs + (size_t)(tag % kSlotsH) * I;
@@ -457,6 +488,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     hs_val = silu_f(a) * u;
   }
 
+  QMOE_PT(4);
   // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the
   //         logits' bits mapped to an order-preserving u32 (-0 counts as +0).
   //         (a) every thread polls its logits; the largest key of each wave;
@@ -498,6 +530,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     const uint32_t wmax = wave_max_u32(lmax);
     if (lane == 0) s_wmax[wv] = wmax;
     __syncthreads();
+  QMOE_PT(5);
     uint32_t L;
     {
       const uint32_t mi = lane < kLW ? s_wmax[lane] : 0u;
@@ -538,6 +571,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     }
   }
   __syncthreads();
+  QMOE_PT(6);
   int eidx[kFusedMaxK];
   float elog[kFusedMaxK];
 #pragma unroll
@@ -623,6 +657,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     dsc[1 + m] = ld_stream4(reinterpret_cast<const uint32_t*>(blk + A.off_dsb) + (int64_t)rb * GI +
                             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
   }
+  QMOE_PT(7);
   // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step (the first
   //         step outside the loop, so that its dots wait for their own rows only,
   //         not for the down rows issued after them)
@@ -647,6 +682,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // the issue only.  Waiting for the stores' acknowledgement first would cost
   // ~0.5 us here; the flag may instead become visible before some of them, and
   // the reader re-reads any word that still has an old tag.
+  QMOE_PT(8);
   __builtin_amdgcn_s_barrier();
   if (tx < 8) tag_put(Lp.flags + wg * kLine + tx, 0.f, tag);
   // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
@@ -664,12 +700,14 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     }
   }
   __syncthreads();
+  QMOE_PT(9);
   // Every workgroup has read the epoch before tagging its flag: advance it.
   if (wg == 0 && tx == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
       hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag, ok_all);
   __syncthreads();
+  QMOE_PT(10);
   if constexpr (STACK) {
     // the next layer's loads that do not depend on its input: the shared-gate
     // vector, the norm weight, the first router rows and the shared expert's rows.
@@ -691,6 +729,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // two vectors; unused routed slots hold stale values whose planes are not read)
   prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, tx, kLB);
   __syncthreads();
+  QMOE_PT(11);
   // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
   const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
   if (lane == 63) s_rv[wv] = gpart;
@@ -738,6 +777,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     }
   }
   __syncthreads();
+  QMOE_PT(12);
   if ((int)tx < kRB && row0 + (int)tx < H) {
     float gs = 0.f;
 #pragma unroll
@@ -811,7 +851,9 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     for (int i = 0; i < CPLR; ++i) rq[i] = rqN[i];
   }
   }  // layers
+  QMOE_PT(13);
   if (!ok_all) flag_status(A.ctrl, 1u);
+  QMOE_PT_STORE();
 }
 
 template <int BITS, int H, int I>
@@ -1068,3 +1110,10 @@ hipError_t launch_stack(const qmoe_layer* Ls, const float* const* norm_w, int n,
 }
 
 }  // namespace qmoe
+
+#ifdef QMOE_PHASE_PROBE
+// the recorded phase timestamps: [64 calls][512 workgroups][16 phases] of uint32
+extern "C" int qmoe_phase_probe_read(void* dst) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(qmoe::g_phase), sizeof(qmoe::g_phase));
+}
+#endif
