@@ -18,6 +18,9 @@ Workloads (all weights 4-bit unless noted; H = 4096, I = 1024, group 64):
   --config 6            one full-attention decode token (32 query heads over 2 KV
                         heads of 256, context 8192, fp32 caches) on a ring of 16
                         caches; a step is one call
+  --config 7            the config-1 layer with its routed experts in pinned host
+                        memory and a 256-slot HBM cache (host-tier offload); a step
+                        is one token
 Inputs are synthetic (seeded Philox streams generated in HBM); weights and
 activations are resident in HBM before the timed region starts.  Steps are
 enqueued as replays of HIP graphs, so the host never synchronises inside the
@@ -730,12 +733,106 @@ def device_info():
     return info
 
 
+def run_offload_bench(args, torch, q, synth):
+    """Host-tier offload: the config-1 layer with its 512 routed experts in pinned
+    host memory and an HBM cache of 256 expert slots (half the layer: a model twice
+    the size of HBM).  A step is one token (fresh x each), waiting on the host for
+    its routing as the offload path does.  Also measured: the host-to-device copy
+    rate alone, the resident fused layer alone, and the two at once on separate
+    streams (whether DMA and compute slow each other on this GPU)."""
+    import numpy as np
+    seed, slots = 1001, 256
+    W = LayerWorkload(seed, 0, 4, torch, q, synth)
+    hbuf = torch.empty(W.routed.buf.numel(), dtype=torch.uint8, pin_memory=True)
+    hbuf.copy_(W.routed.buf)
+    torch.cuda.synchronize()
+    hp = q.ExpertPool(hbuf, E, H, I, 4, W.routed.stride)
+    off = q.Offload(hp, slots)
+    L_off = q.Layer(hp, W.shared, W.router, W.gate, K)
+    n_tok = 256
+    X = make_x_ring(torch, synth, seed, n_tok)
+    out = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.qmoe_offload_workspace_bytes(L_off), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    warm = min(max(args.warmup, 64), n_tok)
+    for t in range(warm):  # fills the cache to its steady state
+        q.moe_layer_forward_offload(off, L_off, X[t % n_tok], out=out, idx=idx, w=w, ws=ws, copy_stream=cs)
+    torch.cuda.synchronize()
+    st0 = off.stats()
+    steps = max(1, min(args.steps, 4096))
+    t0 = time.perf_counter()
+    for t in range(steps):
+        q.moe_layer_forward_offload(off, L_off, X[t % n_tok], out=out, idx=idx, w=w, ws=ws, copy_stream=cs)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st1 = off.stats()
+    hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+    copied = st1["bytes_copied"] - st0["bytes_copied"]
+    # the copy rate alone: 64 expert blocks host -> HBM slots on the copy stream
+    eb = hp.layout["total"]
+    rng = np.random.default_rng(7)
+    picks = rng.integers(0, E, 64)
+
+    def copies(stream):
+        with torch.cuda.stream(stream):
+            for i, e in enumerate(picks):
+                off.slot_mem[(i % slots) * hp.stride:(i % slots) * hp.stride + eb].copy_(
+                    hbuf[int(e) * hp.stride:int(e) * hp.stride + eb], non_blocking=True)
+
+    def timed(fn, stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        return e0, e1
+
+    copies(cs)
+    torch.cuda.synchronize()
+    c0, c1 = timed(lambda: copies(cs), cs)
+    torch.cuda.synchronize()
+    copy_alone = 64 * eb / (c0.elapsed_time(c1) / 1e3) / 1e9
+    # the resident fused layer alone, then together with the copies
+    calls = [(lambda t=t: q.moe_layer_forward(W.L, X[t], X[t], out, idx, w, W.ws)) for t in range(n_tok)]
+    graphs = capture_graphs(torch, calls, n_tok)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    g0, g1 = timed(lambda: [graphs[0].replay() for _ in range(8)], cur)
+    torch.cuda.synchronize()
+    layer_alone = g0.elapsed_time(g1) * 1e3 / (8 * n_tok)
+    c0, c1 = timed(lambda: copies(cs), cs)
+    g0, g1 = timed(lambda: [graphs[0].replay() for _ in range(8)], cur)
+    torch.cuda.synchronize()
+    copy_both = 64 * eb / (c0.elapsed_time(c1) / 1e3) / 1e9
+    layer_both = g0.elapsed_time(g1) * 1e3 / (8 * n_tok)
+    off.close()
+    per_tok = layer_bytes(4)
+    tok_s = steps / dt
+    roof = {"bound": "hbm", "achieved": round(per_tok * tok_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBPS, 5), "traffic": None}
+    extra = {"kernel": "moe_layer_forward_offload (router + top-K, host wait, copies on a second stream, "
+                       "shared and routed expert FFN, combine)",
+             "slots": slots, "hit_rate": round(hits / max(1, hits + misses), 4),
+             "misses_per_token": round(misses / steps, 3),
+             "host_to_device_GBps_in_run": round(copied / dt / 1e9, 2),
+             "avg_token_us": round(dt / steps * 1e6, 2),
+             "copy_alone_GBps": round(copy_alone, 2), "copy_with_layer_running_GBps": round(copy_both, 2),
+             "fused_layer_alone_us": round(layer_alone, 3), "fused_layer_with_copies_us": round(layer_both, 3)}
+    return {"value": tok_s, "unit": "tokens/s (one offloaded layer)", "steps": steps, "dt": dt, "roof": roof,
+            "extra": extra, "cpu": None, "workload": "moe_layer_offload_4bit_512experts_256slots", "bits": 4,
+            "metric": "MoE-layer tokens/s at batch 1, routed experts in pinned host memory (256-slot HBM cache)",
+            "cfg": {"slots": slots, "host_pool_GB": round(hbuf.numel() / 1e9, 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16384)
     ap.add_argument("--warmup", type=int, default=1024)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--persistent", action="store_true",
@@ -799,6 +896,8 @@ def main():
         r = run_gdn_bench(args, torch, q, synth)
     elif args.config == 6:
         r = run_attn_bench(args, torch, q, synth)
+    elif args.config == 7:
+        r = run_offload_bench(args, torch, q, synth)
     else:
         r = run_batched_bench(args, torch, q, synth)
     r["extra"].update(extra0)

@@ -58,6 +58,10 @@ class LayerC(ctypes.Structure):
                 ("shared_gate", ctypes.c_void_p), ("top_k", ctypes.c_int32)]
 
 
+class OffloadStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("calls", "hits", "misses", "bytes_copied")]
+
+
 _vp, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
 _SIGS = {
     "qmoe_expert_layout": ([_i32, _i32, _i32, ctypes.POINTER(ExpertOffsets)], ctypes.c_int),
@@ -79,6 +83,12 @@ _SIGS = {
     "moe_stack_forward": ([ctypes.POINTER(LayerC), ctypes.POINTER(_vp), _i32, _f32, _vp, _vp, _vp, _vp,
                            _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
     "qmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerC), _i32], _sz),
+    "qmoe_offload_create": ([ctypes.POINTER(ExpertPoolC), _i32, _vp, ctypes.POINTER(_vp)], ctypes.c_int),
+    "qmoe_offload_destroy": ([_vp], ctypes.c_int),
+    "qmoe_offload_get_stats": ([_vp, ctypes.POINTER(OffloadStats)], ctypes.c_int),
+    "qmoe_offload_workspace_bytes": ([ctypes.POINTER(LayerC)], _sz),
+    "moe_layer_forward_offload": ([_vp, ctypes.POINTER(LayerC), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp],
+                                  ctypes.c_int),
     "qmoe_stream_read": ([_vp, ctypes.c_int64, ctypes.c_uint32, _vp, _vp], ctypes.c_int),
     "attn_decode_step_qgate": ([_vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -437,6 +447,63 @@ def attn_decode_step_qgate(qg, k, v, k_cache, v_cache, pos, theta=1e7, rot_dim=N
         pos, theta, rot_dim, _ptr(o, torch.float32, "o"), _ptr(gate, torch.float32, "gate"),
         _ptr(ws, None, "ws"), ws.numel(), _stream()), "attn_decode_step_qgate")
     return o, gate
+
+
+class Offload:
+    """A host-tier expert cache: the routed experts in pinned host memory (an
+    ExpertPool whose buf is a pinned CPU tensor) and n_slots expert slots in HBM.
+    Destroyed with the object (or by close())."""
+
+    def __init__(self, host_pool: ExpertPool, n_slots: int, slot_mem: torch.Tensor | None = None):
+        if host_pool.buf.is_cuda or not host_pool.buf.is_pinned():
+            raise ValueError("the host pool must be a pinned CPU tensor")
+        self.host_pool = host_pool
+        self.n_slots = n_slots
+        self.slot_mem = slot_mem if slot_mem is not None else torch.empty(
+            n_slots * host_pool.stride, dtype=torch.uint8, device="cuda")
+        if self.slot_mem.numel() < n_slots * host_pool.stride:
+            raise ValueError("slot_mem too small")
+        h = _vp()
+        _check(_lib.qmoe_offload_create(ctypes.byref(host_pool.c()), n_slots, _ptr(self.slot_mem, None, "slot_mem"),
+                                        ctypes.byref(h)), "qmoe_offload_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.qmoe_offload_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def stats(self) -> dict:
+        st = OffloadStats()
+        _check(_lib.qmoe_offload_get_stats(self._h, ctypes.byref(st)), "qmoe_offload_get_stats")
+        return {n: int(getattr(st, n)) for n, _ in OffloadStats._fields_}
+
+
+def qmoe_offload_workspace_bytes(layer: Layer) -> int:
+    return int(_lib.qmoe_offload_workspace_bytes(ctypes.byref(layer.c())))
+
+
+def moe_layer_forward_offload(off: Offload, layer: Layer, x, residual=None, out=None, idx=None, w=None,
+                              ws=None, copy_stream=None):
+    """One layer whose routed experts are in off's host pool (layer.routed describes
+    that pool).  Returns (out, idx, w).  Waits on the host for the routing."""
+    residual = residual if residual is not None else x
+    dev = x.device
+    out = out if out is not None else torch.empty_like(x)
+    idx = idx if idx is not None else torch.empty(layer.top_k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(layer.top_k, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(qmoe_offload_workspace_bytes(layer), dtype=torch.uint8, device=dev)
+    cs = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+    _check(_lib.moe_layer_forward_offload(off._h, ctypes.byref(layer.c()), _ptr(x, torch.float32, "x"),
+                                          _ptr(residual, torch.float32, "residual"),
+                                          _ptr(out, torch.float32, "out"), _ptr(idx, torch.int32, "idx"),
+                                          _ptr(w, torch.float32, "w"), _ptr(ws, None, "ws"), ws.numel(),
+                                          _stream(), cs), "moe_layer_forward_offload")
+    return out, idx, w
 
 
 def qmoe_stream_read(buf, nbytes=None, key=0xA5A5A5A5, sink=None):

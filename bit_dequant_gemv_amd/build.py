@@ -55,7 +55,7 @@ def _library(srcs, out, extra, verbose, jobs, build_subdir="_build"):
 
 def build_qmoe(verbose=False, jobs=None):
     csrc = os.path.join(HERE, "csrc")
-    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip", "attn.hip", "noalloc.hip", "stream.hip")]
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip", "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
     return _library(srcs, os.path.join(HERE, "libqmoe.so"),
                     ["-I", os.path.join(ROOT, "include"), "-I", csrc], verbose,
                     jobs or min(8, os.cpu_count() or 4))
@@ -67,7 +67,7 @@ def build_probe(verbose=False, jobs=None):
     Not part of the product build."""
     csrc = os.path.join(HERE, "csrc")
     srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip",
-                                            "attn.hip", "noalloc.hip", "stream.hip")]
+                                            "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
     return _library(srcs, os.path.join(HERE, "libqmoe_probe.so"),
                     ["-I", os.path.join(ROOT, "include"), "-I", csrc, "-DQMOE_PHASE_PROBE"], verbose,
                     jobs or min(8, os.cpu_count() or 4), build_subdir="_build_probe")

@@ -411,6 +411,65 @@ int qmoe_stream_read(const void* buf, int64_t bytes, uint32_t key, uint32_t* sin
                     "qmoe_stream_read launch");
 }
 
+int qmoe_offload_create(const qmoe_expert_pool* host_pool, int32_t n_slots, void* slot_mem,
+                        qmoe_offload** out) {
+  if (!out) return fail(QMOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_pool(host_pool, "host_pool");
+  if (rc) return rc;
+  if (n_slots < 1) return fail(QMOE_ESHAPE, "n_slots must be >= 1");
+  if (!slot_mem) return fail(QMOE_EINVAL, "slot_mem is NULL");
+  if (!aligned(slot_mem, 256)) return fail(QMOE_EALIGN, "slot_mem must be 256-byte aligned");
+  rc = qmoe::offload_create(*host_pool, n_slots, slot_mem, out);
+  if (rc) return fail(rc, "could not create the offload handle (pinned staging or events)");
+  return QMOE_OK;
+}
+
+int qmoe_offload_destroy(qmoe_offload* handle) {
+  if (!handle) return fail(QMOE_EINVAL, "handle is NULL");
+  qmoe::offload_destroy(handle);
+  return QMOE_OK;
+}
+
+int qmoe_offload_get_stats(const qmoe_offload* handle, qmoe_offload_stats* out) {
+  if (!handle || !out) return fail(QMOE_EINVAL, "NULL pointer");
+  qmoe::offload_stats(handle, out);
+  return QMOE_OK;
+}
+
+size_t qmoe_offload_workspace_bytes(const qmoe_layer* L) {
+  if (!L || L->top_k < 1 || L->routed.num_experts < 1 || L->routed.hidden < 1 || L->routed.inter < 1)
+    return 0;
+  return qmoe::offload_workspace_bytes(*L);
+}
+
+int moe_layer_forward_offload(qmoe_offload* handle, const qmoe_layer* L, const float* x,
+                              const float* residual, float* out, int32_t* topk_idx, float* topk_w,
+                              void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+  if (!handle) return fail(QMOE_EINVAL, "handle is NULL");
+  if (!L) return fail(QMOE_EINVAL, "layer is NULL");
+  // the routed pool's base is unused (the experts are in the handle's host pool)
+  qmoe_layer Lc = *L;
+  Lc.routed.base = qmoe::offload_host_pool(handle).base;
+  int rc = check_layer(&Lc);
+  if (rc) return rc;
+  const qmoe_expert_pool& hp = qmoe::offload_host_pool(handle);
+  if (L->routed.num_experts != hp.num_experts || L->routed.hidden != hp.hidden ||
+      L->routed.inter != hp.inter || L->routed.bits != hp.bits)
+    return fail(QMOE_ESHAPE, "the layer's routed shape differs from the handle's host pool");
+  if (L->top_k > qmoe::offload_slots(handle)) return fail(QMOE_ESHAPE, "n_slots must be >= top_k");
+  if ((rc = check_vec(x, "x"))) return rc;
+  if (!residual || !out || !topk_idx || !topk_w) return fail(QMOE_EINVAL, "NULL pointer");
+  if (out == x) return fail(QMOE_EINVAL, "out must not alias x");
+  const size_t need = qmoe_offload_workspace_bytes(L);
+  if (!ws || ws_bytes < need) return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(QMOE_EALIGN, "ws must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t cs = copy_stream ? static_cast<hipStream_t>(copy_stream) : s;
+  return hip_status(qmoe::offload_layer(handle, Lc, x, residual, out, topk_idx, topk_w, ws, s, cs),
+                    "moe_layer_forward_offload");
+}
+
 const char* qmoe_strerror(int status) {
   switch (status) {
     case QMOE_OK: return "ok";

@@ -82,6 +82,17 @@ hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t key, uint32_t* sink,
                               hipStream_t s);
 
+// host-tier expert offload (offload.cpp)
+size_t offload_workspace_bytes(const qmoe_layer& L);
+int offload_create(const qmoe_expert_pool& host, int32_t n_slots, void* slot_mem, qmoe_offload** out);
+void offload_destroy(qmoe_offload* o);
+void offload_stats(const qmoe_offload* o, qmoe_offload_stats* s);
+const qmoe_expert_pool& offload_host_pool(const qmoe_offload* o);
+int32_t offload_slots(const qmoe_offload* o);
+hipError_t offload_layer(qmoe_offload* o, const qmoe_layer& L, const float* x, const float* residual,
+                         float* out, int32_t* idx, float* w, void* ws, hipStream_t s,
+                         hipStream_t copy_stream);
+
 // compute units of the current device (cached per device); 0 if it cannot be read
 int device_cus();
 

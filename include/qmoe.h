@@ -312,6 +312,48 @@ int attn_decode_step_qgate(const float* qg, const float* k, const float* v, cons
 size_t qmoe_attn_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t Tmax);
 
 /*
+ * Host-tier expert offload ([PK] "SSD 전문가 스트리밍과 "OS 신뢰" 원칙" and
+ * "레이어당 파이프라인 상세 구조": the selected experts of each layer are read from
+ * storage after a host-side top-K, the popular ones kept by a cache).  For layers
+ * whose routed experts do not fit in HBM: the routed pool lives in pinned host
+ * memory, and an LRU cache of n_slots expert slots in HBM keeps the recently used
+ * ones.  Per token: router + top-K on the GPU; the K indices come back to the host
+ * (the only synchronisation, on an event); the shared expert's FFN runs meanwhile;
+ * missing experts are copied host-to-device on copy_stream into the least recently
+ * used slots; then the routed FFN on the slots and the combine.  The result equals
+ * moe_layer_forward's up to rounding (the stand-alone kernels run, not the fused
+ * one).
+ *
+ * qmoe_offload_create: host_pool describes the routed experts with base = a
+ *   PINNED HOST pointer (hipHostMalloc), the same stride rules as a device pool;
+ *   slot_mem: device memory of n_slots * host_pool->stride bytes, 256-byte aligned,
+ *   owned by the caller; n_slots >= 1.  *out receives a handle (host memory the
+ *   library allocates here, freed by qmoe_offload_destroy).
+ * moe_layer_forward_offload: L->shared, L->router, L->shared_gate and L->top_k are
+ *   used as in moe_layer_forward; L->routed must have the host pool's shape and
+ *   its base is ignored.  x, residual, out, topk_idx, topk_w as in moe_layer_forward.
+ *   ws: device, at least qmoe_offload_workspace_bytes(L), 256-byte aligned (scratch).
+ *   copy_stream: a hipStream_t for the copies (NULL: stream).  The call waits on the
+ *   host for the router's indices, so it cannot be captured in a graph.  Calls on
+ *   one handle must come from one host thread at a time.  n_slots must be >= top_k.
+ * Errors: QMOE_EINVAL / QMOE_EALIGN / QMOE_ESHAPE for bad arguments, QMOE_EHIP for a
+ * runtime failure.  qmoe_offload_get_stats: calls, expert hits and misses, bytes
+ * copied since creation.
+ */
+typedef struct qmoe_offload qmoe_offload;
+typedef struct {
+  uint64_t calls, hits, misses, bytes_copied;
+} qmoe_offload_stats;
+int qmoe_offload_create(const qmoe_expert_pool* host_pool, int32_t n_slots, void* slot_mem,
+                        qmoe_offload** out);
+int qmoe_offload_destroy(qmoe_offload* handle);
+int qmoe_offload_get_stats(const qmoe_offload* handle, qmoe_offload_stats* out);
+size_t qmoe_offload_workspace_bytes(const qmoe_layer* L);
+int moe_layer_forward_offload(qmoe_offload* handle, const qmoe_layer* L, const float* x,
+                              const float* residual, float* out, int32_t* topk_idx, float* topk_w,
+                              void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/*
  * RMSNorm ([PK] Metal shaders: two-stage RMS normalisation):
  *   out = v / sqrt(mean(v^2) + eps) * w;  v, w, out: device float [n]; out may alias v.
  */

@@ -144,3 +144,21 @@ def test_workspace_grows_with_batch():
     b = lib.qmoe_workspace_bytes(ctypes.byref(L), 64)
     assert b > a > (512 + 1) * 8
     assert b % 256 == 0 and a % 256 == 0
+
+
+def test_offload_handle_arguments_are_checked_on_the_host():
+    import bit_dequant_gemv_amd as q
+    lib = q.raw_lib()
+    h = ctypes.c_void_p()
+    pool = q.ExpertPoolC(0, 1 << 23, 4, 1024, 256, 4)  # null base
+    assert lib.qmoe_offload_create(ctypes.byref(pool), 2, ctypes.c_void_p(256), ctypes.byref(h)) == q.QMOE_EINVAL
+    pool = q.ExpertPoolC(4096, 1 << 23, 4, 1024, 256, 4)
+    assert lib.qmoe_offload_create(ctypes.byref(pool), 0, ctypes.c_void_p(256), ctypes.byref(h)) == q.QMOE_ESHAPE
+    assert lib.qmoe_offload_create(ctypes.byref(pool), 2, None, ctypes.byref(h)) == q.QMOE_EINVAL
+    assert lib.qmoe_offload_create(ctypes.byref(pool), 2, ctypes.c_void_p(100), ctypes.byref(h)) == q.QMOE_EALIGN
+    assert lib.qmoe_offload_create(ctypes.byref(pool), 2, ctypes.c_void_p(256), None) == q.QMOE_EINVAL
+    assert lib.qmoe_offload_destroy(None) == q.QMOE_EINVAL
+    assert lib.moe_layer_forward_offload(None, None, None, None, None, None, None, None, 0, None, None) \
+        == q.QMOE_EINVAL
+    L = q.LayerC(pool, q.ExpertPoolC(4096, 1 << 23, 1, 1024, 256, 4), 256, 256, 4)
+    assert lib.qmoe_offload_workspace_bytes(ctypes.byref(L)) > 4 * 1024 * 4
