@@ -64,13 +64,25 @@ def layer_bytes(bits: int) -> int:
     return E * H * 2 + (K + 1) * expert_bytes(bits) + H * 2 + 3 * H * 4
 
 
-def sources_sha() -> str:
-    """Hash of the kernel sources' code: comment-only lines and blank lines are
-    left out, so editing a comment does not invalidate counters taken on the
-    same code."""
+# the kernel sources each counter record depends on (a change elsewhere leaves it valid)
+TRAFFIC_SOURCES = {
+    "k_layer_w4": ["layer.hip", "qmoe_device.h"],
+    "k_layer_w2": ["layer.hip", "qmoe_device.h"],
+    "k_layer_w4_stack60": ["layer.hip", "qmoe_device.h"],
+    "expert_ffn_w4": ["kernels.hip", "qmoe_device.h"],
+    "batched64_w4": ["batched.hip", "kernels.hip", "qmoe_device.h"],
+    "k_gdn": ["gdn.hip"],
+    "k_attn_part": ["attn.hip"],
+}
+
+
+def sources_sha(files=None) -> str:
+    """Hash of the kernel sources' code (all of csrc/, or the given files):
+    comment-only lines and blank lines are left out, so editing a comment does not
+    invalidate counters taken on the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_dequant_gemv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
             for line in open(os.path.join(csrc, f), encoding="utf-8"):
                 t = line.strip()
@@ -81,14 +93,14 @@ def sources_sha() -> str:
 
 def traffic_from_profiles(kernel_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current sources of that kernel; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
         rec = d.get(kernel_key)
-        if rec and rec.get("sources_sha") == sources_sha():
+        if rec and rec.get("sources_sha") == sources_sha(TRAFFIC_SOURCES.get(kernel_key)):
             return rec.get("bytes_per_launch")
     except Exception:
         return None
@@ -571,11 +583,13 @@ def run_stack_bench(args, torch, q, synth):
             raise RuntimeError("fused layer kernel reported a time-out")
     per_tok = n_layers * (layer_bytes(4) + H * 4)  # + the RMSNorm weight
     tok_s = steps / dt
+    # per launch (one layer): its bytes over the average layer time; the same ratio
+    # as a whole token's bytes over the token's time
     roof = {"bound": "hbm", "achieved": round(per_tok * tok_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
-            "traffic": None}
+            "traffic": traffic_from_profiles("k_layer_w4_stack60")}
     kern = ("k_stack, 32 + 28 layers per launch" if args.persistent else "k_layer x60 per token")
-    extra = {"kernel": kern + ", RMSNorm fused (roofline over the token)",
+    extra = {"kernel": kern + ", RMSNorm fused (roofline per layer launch; traffic per launch)",
              "bytes_per_token": per_tok, "layer_evals_per_s": round(tok_s * n_layers, 1),
              "resident_GB": round(sum(W.routed.buf.numel() + W.shared.buf.numel() for W in layers) / 1e9, 1)}
     cpu = None
@@ -641,7 +655,8 @@ def run_batched_bench(args, torch, q, synth):
     per_batch = E * H * 2 + (d_avg + 1) * expert_bytes(4) + H * 2 + 3 * T * H * 4
     batch_s = dt / steps
     roof = {"bound": "hbm", "achieved": round(per_batch / batch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(per_batch / batch_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None}
+            "unit": "GB/s", "frac": round(per_batch / batch_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles("batched64_w4")}
     extra = {"kernel": "moe_layer_forward_batched (router, grouping, grouped gate/up, down, combine), "
                        "roofline over the whole call", "distinct_experts_avg": round(d_avg, 1),
              "bytes_per_batch": int(per_batch), "avg_batch_us": round(batch_s * 1e6, 2)}
@@ -695,6 +710,22 @@ def run_phase_probe(args, torch, q, synth):
     print(json.dumps({"phase_probe": True, "bits": bits, "avg_launch_us": round(dt / (16 * n) * 1e6, 3),
                       "phases_median_us": {name: round(float(med[k, 1]), 3) for k, name in enumerate(PHASES)},
                       "phases_max_us": {name: round(float(med[k, 2]), 3) for k, name in enumerate(PHASES)}}))
+
+
+def launch_bytes(config):
+    """Algorithmic bytes of one launch (or call) of the config's dominant kernel
+    path, the size at which the read-only calibration stream is run."""
+    if config in (1, 2, 3):
+        return layer_bytes(4 if config != 2 else 2)
+    if config == 0:
+        return expert_bytes(4) + 2 * H * 4
+    if config == 4:
+        return E * H * 2 + 203 * expert_bytes(4) + H * 2 + 3 * 64 * H * 4
+    if config == 5:
+        return 2 * 64 * 128 * 128 * 4 + (2 * 64 * 128 * 2 + 2 * 64) * 4
+    if config == 6:
+        return 2 * 2 * 8192 * 256 * 4 + 2 * 32 * 256 * 4 + 2 * 2 * 256 * 4
+    return None
 
 
 def device_info():
@@ -900,6 +931,13 @@ def main():
         r = run_offload_bench(args, torch, q, synth)
     else:
         r = run_batched_bench(args, torch, q, synth)
+    if "attainable_GBps_same_bytes_per_launch" not in extra0 and r["roof"].get("unit") == "GB/s" \
+            and launch_bytes(args.config):
+        nb = launch_bytes(args.config)
+        att = list(run_stream_calibration(torch, q, [nb]).values())[0]
+        extra0["attainable_GBps_same_bytes_per_launch"] = round(att, 1)
+        extra0["attainable_bytes_per_launch"] = nb
+        extra0["frac_of_attainable_same_bytes"] = round(r["roof"]["achieved"] / att, 4)
     r["extra"].update(extra0)
     config = r.get("config") or {"workload": r["workload"], "experts": E, "hidden": H, "inter": I,
                                  "top_k": K, "shared_experts": 1, "group": 64, "bits": r["bits"]}
