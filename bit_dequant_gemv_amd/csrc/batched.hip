@@ -1,6 +1,6 @@
 // Batched decode through one MoE layer: T tokens, each routed to its own top-K.
 //
-// Row t of the result equals the batch-1 layer on token t.  To read each active
+// Row t of the result is the batch-1 layer on token t (up to the order of fp32 sums).  To read each active
 // expert's weights once per batch, the (token, k) pairs are grouped by expert:
 // a histogram over the routed expert ids, an exclusive scan into per-expert
 // offsets, and a stable scatter of the pair ids (pair p = t*K + k, in ascending
@@ -9,9 +9,11 @@
 // (the shared one always) is spread over many workgroups.  The fixed-point x
 // planes of every token are built once; a workgroup then loads its block of an
 // expert's gate/up rows into registers and applies them to each token of its
-// chunk.  The SwiGLU outputs h get planes of their own, the down rows go the same
-// way, and a per-token combine adds the weighted routed outputs, the
-// sigmoid-gated shared output and the residual.
+// chunk.  The shared expert's gate/up chunks (32 tokens each) run on the matrix
+// cores instead, as fp32 GEMM tiles of dequantised weights by the tokens' x.  The
+// SwiGLU outputs h get planes of their own, the down rows go the same way as the
+// routed gate/up rows, and a per-token combine adds the weighted routed outputs,
+// the sigmoid-gated shared output and the residual.
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -198,18 +200,191 @@ struct PoolArgsB {
 
 __device__ __forceinline__ int token_of(int p, int T, int K) { return p < T * K ? p / K : p - T * K; }
 
+// ---------------------------------------------------------------------------
+// The shared expert's gate/up chunks on the matrix cores.
+//
+// A chunk of the shared expert holds up to kChunk tokens, so each of its weight
+// rows meets 32 input columns: a small GEMM, (rows x K) by (K x tokens), where the
+// routed experts' chunks (one or two tokens) stay row dots on the vector ALUs.  The
+// routed chunks keep the row dots because a 16-column tile would be 1/16 used and
+// the per-group scale then costs as many ALU operations as the dots it replaces.
+// The weights are dequantised in fp32, w = fma(code, scale, bias) (one rounding of
+// the exact code*scale + bias), and are the A operand of v_mfma_f32_16x16x4_f32;
+// the tokens' fp32 inputs are the B operand.  The products are the fp32 products
+// of a plain float GEMV; only the order of the fp32 sums differs.
+//
+// Operands of the 16x16x4 fp32 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16]
+// and gets D[4*(l/16) + v][l%16] in result register v.  The four k slots of a step
+// are the four lane groups g = l/16; group g walks chunk 4*kb + g of the row (its
+// 16-byte code load), one code per step, so a step covers code n of four chunks at
+// once and a lane's B value is its column's input at that same position.
+// The waves split the chunks (wave w takes chunks 4*kb + g with kb = w mod 4) and
+// add their 16x32 partial tiles through LDS; wave 0 writes the results.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMfmaCols = 16;  // columns (tokens) per MFMA tile
+static_assert(kChunk == 2 * kMfmaCols, "a shared chunk is two column tiles");
+static_assert(kBB == 256, "four waves share the chunks of a row");
+
+template <int NM>
+constexpr int mfma_red_floats() {  // LDS for the cross-wave sum: waves 1..3, NM x 2 tiles x 4 x 64
+  return 3 * NM * 2 * 4 * 64;
+}
+
+// NM = 2: gate and up rows, SwiGLU into dst; NM = 1: down rows into dst.
+// codes[m] / sb[m]: the matrix's code rows (K*BITS/8 bytes each) and scale|bias
+// words (K/64 each).  Output rows [row0, row_end).  Column c < p1 - p0 of the chunk
+// is pair pair_list[p0 + c]; its input row is src + in_row * src_ld with in_row its
+// token (src_token) or the pair itself, its output row dst + pair * dst_ld.
+template <int BITS, int NM>
+__device__ __forceinline__ void shared_chunk_mfma(const uint8_t* const (&codes)[NM],
+                                                  const uint32_t* const (&sb)[NM], int K,
+                                                  int row0, int row_end, const float* src,
+                                                  int64_t src_ld, bool src_token, float* dst,
+                                                  int64_t dst_ld, const int* pair_list, int p0,
+                                                  int p1, int T, int Kt, float* red) {
+  constexpr int EPC = QTraits<BITS>::EPC, EPW = QTraits<BITS>::EPW, CPG = QTraits<BITS>::CPG;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  constexpr int PIECES = EPC / 8;  // eight codes (two float4 of input) per piece
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int C = K / EPC, GW = K / kGroup;
+  const int64_t rb = (int64_t)K * BITS / 8;
+  const float* xs[2];
+  int pc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int c = p0 + tt * kMfmaCols + r;
+    pc[tt] = c < p1 ? pair_list[c] : -1;
+    xs[tt] = pc[tt] < 0 ? nullptr : src + (int64_t)(src_token ? token_of(pc[tt], T, Kt) : pc[tt]) * src_ld;
+  }
+  const int n_kb = (C + 3) / 4;  // chunk blocks of the row, four chunks each
+  for (int rt0 = row0; rt0 < row_end; rt0 += 16) {
+    const int row = rt0 + r;
+    const bool rok = row < row_end;
+    f32x4_t acc[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[m][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kb = wv; kb < n_kb; kb += 4) {
+      const int ch = 4 * kb + g;
+      const bool cok = ch < C;
+      uint4 q[NM];
+      float sc[NM], bi[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (cok && rok) {
+          q[m] = ld_stream16(codes[m] + row * rb + 16 * ch);
+          const uint32_t s = ld_stream4(sb[m] + (int64_t)row * GW + ch / CPG);
+          sc[m] = bf16_lo(s);
+          bi[m] = bf16_hi(s);
+        } else {  // no row or no chunk: zero weights
+          q[m] = make_uint4(0u, 0u, 0u, 0u);
+          sc[m] = bi[m] = 0.f;
+        }
+      }
+      // a piece: eight codes and two float4 of each column's input.  The loop stays
+      // rolled and loads one piece at a time, so this path needs few registers: it
+      // shares the kernel (and its register count) with the routed experts' row dots,
+      // whose waves hide its load latency
+#pragma unroll 1
+      for (int pi = 0; pi < PIECES; ++pi) {
+        float b[2][8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (xs[tt] && cok) {
+            const float4* xp = reinterpret_cast<const float4*>(xs[tt] + ch * EPC + 8 * pi);
+            const float4 u = xp[0], v = xp[1];
+            b[tt][0] = u.x, b[tt][1] = u.y, b[tt][2] = u.z, b[tt][3] = u.w;
+            b[tt][4] = v.x, b[tt][5] = v.y, b[tt][6] = v.z, b[tt][7] = v.w;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[tt][j] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            // code j of the piece: the low 8*BITS bits of the current word
+            const float a = fmaf((float)((q[m].x >> (BITS * j)) & MASK), sc[m], bi[m]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+              acc[m][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[tt][j], acc[m][tt], 0, 0, 0);
+          }
+        }
+        // eight codes consumed: the next word moves in (4-bit), or the word's upper half (2-bit)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (BITS == 4 || (pi & 1)) q[m] = make_uint4(q[m].y, q[m].z, q[m].w, 0u);
+          else q[m].x >>= 16;
+        }
+      }
+    }
+    // the four waves' partial tiles: 1..3 through LDS into wave 0
+    if (wv > 0) {
+      float* o = red + (wv - 1) * (NM * 2 * 4 * 64);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[((m * 2 + tt) * 4 + v) * 64 + lane] = acc[m][tt][v];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const float* o = red + w * (NM * 2 * 4 * 64);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[m][tt][v] += o[((m * 2 + tt) * 4 + v) * 64 + lane];
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if (pc[tt] < 0) continue;
+        float* d = dst + (int64_t)pc[tt] * dst_ld;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int orow = rt0 + 4 * g + v;
+          if (orow < row_end) {
+            if constexpr (NM == 2) d[orow] = silu_f(acc[0][tt][v]) * acc[1][tt][v];
+            else d[orow] = acc[0][tt][v];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+
 // grid (row blocks, group chunks): a wave loads NR gate/up row pairs once and
 // applies them to every token of its chunk, taking each token's prepared planes.
 template <int BITS, int LG, int CPL, int NR>
 __global__ __launch_bounds__(kBB) void k_bgateup(PoolArgsB P, GroupTables G,
                                                  const uint32_t* __restrict__ xp,
+                                                 const float* __restrict__ xf,
                                                  float* __restrict__ h, int rows_per_block) {
   constexpr int RPW = 64 / LG;
+  __shared__ float red[mfma_red_floats<2>()];
   // groups in reverse: the shared expert's chunks (the most tokens each) start first
   const int ng = G.n_groups[0];
   if ((int)blockIdx.y >= ng) return;
   const int gi = ng - 1 - (int)blockIdx.y;
   const int e = G.group_expert[gi];
+  if (e == -1) {  // a shared-expert chunk (uniform per workgroup): matrix cores, fp32 x
+    const uint8_t* const cm[2] = {P.sblk + P.off_g, P.sblk + P.off_u};
+    const uint32_t* const sm[2] = {reinterpret_cast<const uint32_t*>(P.sblk + P.off_gsb),
+                                   reinterpret_cast<const uint32_t*>(P.sblk + P.off_usb)};
+    const int row0 = (int)blockIdx.x * rows_per_block;
+    shared_chunk_mfma<BITS, 2>(cm, sm, P.H, row0, min(P.I, row0 + rows_per_block), xf, P.H, true, h,
+                               P.I, G.pair_list, G.group_off[gi], G.group_off[gi + 1], P.T, P.K, red);
+    return;
+  }
   const bool eok = e == -1 || (unsigned)e < (unsigned)P.E;
   const uint8_t* blk = e == -1 ? P.sblk : P.rbase + (eok ? (int64_t)e * P.rstride : 0);
   const int C = P.H * BITS / 128, G_ = P.H / kGroup;
@@ -261,6 +436,9 @@ __global__ __launch_bounds__(kBB) void k_bgateup(PoolArgsB P, GroupTables G,
   }
 }
 
+// (the shared expert's down rows stay row dots: measured on the 64-token batch, the
+// matrix-core branch here made the batch slower, 316.9 against 312.3 us, since its
+// chunk of 64 rows x 1024 is short and waits on its inputs' load latency)
 template <int BITS, int LG, int CPL, int NR>
 __global__ __launch_bounds__(kBB) void k_bdown(PoolArgsB P, GroupTables G,
                                                const uint32_t* __restrict__ hp,
@@ -366,15 +544,15 @@ __global__ __launch_bounds__(kBB) void k_bcombine(const float* __restrict__ y,
 static_assert(kCombineCols == 4 * kBB, "one float4 of columns per thread");
 
 template <int BITS, int LG, int CPL>
-void run_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp, float* h,
-                 hipStream_t s) {
+void run_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp,
+                 const float* xf, float* h, hipStream_t s) {
   constexpr int RPW = 64 / LG;
   // four gate/up row pairs per wave (measured on the 64-token batch: 324 us against
   // 328 with two pairs, 389 with eight, 402 with one)
   constexpr int NR = 4;
   const int rpb = (kBB / 64) * NR * RPW;
   hipLaunchKernelGGL((k_bgateup<BITS, LG, CPL, NR>), dim3(ceil_div(P.I, rpb), gm), dim3(kBB), 0, s,
-                     P, G, xp, h, rpb);
+                     P, G, xp, xf, h, rpb);
 }
 
 template <int BITS, int LG, int CPL>
@@ -388,18 +566,18 @@ void run_bdown(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t*
 }
 
 template <int BITS>
-void dispatch_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp, float* h,
-                      hipStream_t s) {
+void dispatch_bgateup(const PoolArgsB& P, const GroupTables& G, int gm, const uint32_t* xp,
+                      const float* xf, float* h, hipStream_t s) {
   const int C = P.H * BITS / 128;
-  if (C <= 1) return run_bgateup<BITS, 1, 1>(P, G, gm, xp, h, s);
-  if (C <= 2) return run_bgateup<BITS, 2, 1>(P, G, gm, xp, h, s);
-  if (C <= 4) return run_bgateup<BITS, 4, 1>(P, G, gm, xp, h, s);
-  if (C <= 8) return run_bgateup<BITS, 8, 1>(P, G, gm, xp, h, s);
-  if (C <= 16) return run_bgateup<BITS, 16, 1>(P, G, gm, xp, h, s);
-  if (C <= 32) return run_bgateup<BITS, 32, 1>(P, G, gm, xp, h, s);
-  if (C <= 64) return run_bgateup<BITS, 64, 1>(P, G, gm, xp, h, s);
-  if (C <= 128) return run_bgateup<BITS, 64, 2>(P, G, gm, xp, h, s);
-  return run_bgateup<BITS, 64, 4>(P, G, gm, xp, h, s);
+  if (C <= 1) return run_bgateup<BITS, 1, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 2) return run_bgateup<BITS, 2, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 4) return run_bgateup<BITS, 4, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 8) return run_bgateup<BITS, 8, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 16) return run_bgateup<BITS, 16, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 32) return run_bgateup<BITS, 32, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 64) return run_bgateup<BITS, 64, 1>(P, G, gm, xp, xf, h, s);
+  if (C <= 128) return run_bgateup<BITS, 64, 2>(P, G, gm, xp, xf, h, s);
+  return run_bgateup<BITS, 64, 4>(P, G, gm, xp, xf, h, s);
 }
 
 template <int BITS>
@@ -471,11 +649,11 @@ hipError_t launch_layer_batched(const qmoe_layer& L, const float* x, const float
   const int gm = max_groups(T, K);
   const int npairs = T * K + T;
   if (bits == 4) {
-    dispatch_bgateup<4>(P, G, gm, xp, h, s);
+    dispatch_bgateup<4>(P, G, gm, xp, x, h, s);
     run_prep<4>(h, npairs, I, hp, s);
     dispatch_bdown<4>(P, G, gm, hp, y, s);
   } else {
-    dispatch_bgateup<2>(P, G, gm, xp, h, s);
+    dispatch_bgateup<2>(P, G, gm, xp, x, h, s);
     run_prep<2>(h, npairs, I, hp, s);
     dispatch_bdown<2>(P, G, gm, hp, y, s);
   }
