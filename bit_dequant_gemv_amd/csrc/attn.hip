@@ -22,6 +22,7 @@ namespace {
 // keys per LDS tile (16-key tiles, three workgroups per CU, measured slower: 26.8 against
 // 26.0 us at context 8192)
 constexpr int kTK = 32;
+constexpr int kPF = 2;  // float4 of K and of V per thread and tile held in registers
 constexpr int kSPL = 64 / kTK;  // lanes per key in the score phase, each summing D / kSPL dims
 constexpr int kMaxSplit = 2048;  // splits per head: at most ceil(256 / Hkv) <= 256, or T / kTK
 
@@ -75,6 +76,26 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float*
   const bool owns_pos = t0 <= pos && pos < t1;
   float* kg = kc + (int64_t)g * Tmax * D;
   float* vg = vc + (int64_t)g * Tmax * D;
+  // Tile loads go to registers first, kPF float4 of K and of V per thread: the
+  // range's first tile is requested before the rotation angles and the q rows are
+  // prepared, and each later tile as soon as the one before is in LDS, so HBM
+  // latency overlaps that work and the previous tile's scores.  The loads are
+  // unconditional (row and index clamped into the range: a key past the range or
+  // the row at pos, still stale here, is replaced or ignored when the tile is
+  // stored).  One buffer: the 1024-thread workgroup caps a thread at 128 VGPRs,
+  // and a second buffer spilled across the double-precision angle computation.
+  constexpr int TQ = kTK * D / 4;  // float4 of K (and of V) per tile
+  auto issue = [&](int tb, float4 (&rk)[kPF], float4 (&rv)[kPF]) {
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) {
+      const int i = min((int)threadIdx.x + u * nthr, TQ - 1);
+      const int t = min(tb + i / (D / 4), t1 - 1), c4 = i % (D / 4);
+      rk[u] = reinterpret_cast<const float4*>(kg + (int64_t)t * D)[c4];
+      rv[u] = reinterpret_cast<const float4*>(vg + (int64_t)t * D)[c4];
+    }
+  };
+  float4 rk[kPF], rv[kPF];
+  issue(t0, rk, rv);
   const int half = rot_dim / 2;
   for (int i = threadIdx.x; i < half; i += nthr) {
     // in double: pos * theta^(-2i/rot_dim) reaches 1e4 rad and more
@@ -133,20 +154,29 @@ __global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float*
   for (int tb = t0; tb < t1; tb += kTK) {
     const int nk = min(kTK, t1 - tb);
     __syncthreads();  // the previous tile is consumed (and s_q, s_kn, s_vn are written)
-    for (int i = threadIdx.x; i < kTK * D / 4; i += nthr) {
+    // the tile from its registers into LDS (slots past the registers' reach, when
+    // the workgroup has fewer than TQ / kPF threads, are loaded here directly)
+    auto put = [&](int i, float4 kv, float4 vv) {
       const int t = i / (D / 4), c4 = i % (D / 4);
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (tb + t == pos) {  // this token: from LDS (its cache row is written above)
         kv = reinterpret_cast<const float4*>(s_kn)[c4];
         vv = reinterpret_cast<const float4*>(s_vn)[c4];
-      } else if (t < nk) {
-        kv = reinterpret_cast<const float4*>(kg + (int64_t)(tb + t) * D)[c4];
-        vv = reinterpret_cast<const float4*>(vg + (int64_t)(tb + t) * D)[c4];
       }
       *reinterpret_cast<float4*>(s_k + t * KS + 4 * c4) = kv;
       reinterpret_cast<float4*>(s_v)[i] = vv;
+    };
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) {
+      const int i = (int)threadIdx.x + u * nthr;
+      if (i < TQ) put(i, rk[u], rv[u]);
+    }
+    for (int i = (int)threadIdx.x + kPF * nthr; i < TQ; i += nthr) {
+      const int t = min(tb + i / (D / 4), t1 - 1), c4 = i % (D / 4);
+      put(i, reinterpret_cast<const float4*>(kg + (int64_t)t * D)[c4],
+          reinterpret_cast<const float4*>(vg + (int64_t)t * D)[c4]);
     }
     __syncthreads();
+    if (tb + kTK < t1) issue(tb + kTK, rk, rv);  // the next tile, into the freed registers
     // scores: lane (kt, kh) sums part kh of q_h . K_kt
     float sp = 0.f;
     const float* kr = s_k + kt * KS + kh * (D / kSPL);
