@@ -8,10 +8,10 @@
 //   q, k <- rope(q, pos), rope(k, pos)   (rotate-half on the first rot_dim dims)
 //   K[g][pos], V[g][pos] <- k[g], v[g]
 //   o[h] = sum_{t <= pos} softmax_t(q[h] . K[g][t] / sqrt(D)) V[g][t],  g = h / (Hq/Hkv)
-// Two launches: k_attn_part (rotations and cache rows; a workgroup per KV head and
-// key range, one wave per query head of the group, so each key and value row is
-// read from HBM once for the whole group; online softmax over tiles of 32 keys
-// staged in LDS) and k_attn_combine (the ranges' partial results merged).
+// Two launches: k_attn_mma (rotations and cache rows, then the scores and the
+// weighted values of a key range on the matrix cores; a workgroup per KV head and
+// key range, so each key and value row is read from HBM once for the whole query
+// group) and k_attn_combine (the ranges' partial results merged).
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -19,12 +19,7 @@ namespace qmoe {
 
 namespace {
 
-// keys per LDS tile (16-key tiles, three workgroups per CU, measured slower: 26.8 against
-// 26.0 us at context 8192)
-constexpr int kTK = 32;
-constexpr int kPF = 2;  // float4 of K and of V per thread and tile held in registers
-constexpr int kSPL = 64 / kTK;  // lanes per key in the score phase, each summing D / kSPL dims
-constexpr int kMaxSplit = 2048;  // splits per head: at most ceil(256 / Hkv) <= 256, or T / kTK
+constexpr int kMaxSplit = 2048;  // ranges per head: at most ceil(256 / Hkv) <= 256
 
 // a partial result record: acc[D], m, l, padding to a multiple of 16 bytes
 template <int D>
@@ -32,16 +27,6 @@ constexpr int rec() {
   return D + 4;
 }
 
-// Partial attention of the G query heads of KV head g over keys [t0, t1): the
-// running max m, the sum of weights l and the weighted sum of values acc[D], in
-// part[h][split][D + 4] = {acc..., m, l, -, -}.  One wave per query head (measured
-// faster than a wave serving four heads, 25.9 against 33.0 us at context 8192, and
-// than waves reading rows straight from memory for all 16 heads, 31.6 us).
-// RoPE and the cache append are done here too: every workgroup takes the rotation
-// angles of position pos (rot_dim / 2 of them, the same for every head) and rotates
-// its group's q rows into LDS; the workgroup whose range holds pos rotates the new
-// k, writes k and v to row pos of the caches and puts them into its tile directly
-// (no other workgroup reads that row in this call).
 // The query side: q rows of q_stride floats (D, or 2D when the query projection
 // interleaves each head's D query values with its D gate values: the query is the
 // first half of the row); qnw / knw: RMS-normalisation weights [D] of q and k, or
@@ -54,178 +39,306 @@ struct AttnQ {
   float* gate;
 };
 
+// Partial attention of the G <= 16 query heads of KV head g over keys [t0, t1): the
+// running max m, the sum of weights l and the weighted sum of values acc[D], in
+// part[h][split][D + 4] = {acc..., m, l, -, -}, on the matrix cores.  The heads are
+// the 16 columns of v_mfma_f32_16x16x4_f32 tiles (heads past G are zero), so
+// every key and value row is read once per workgroup, from HBM straight into the
+// operand registers, with no LDS staging:
+//   scores  S^T[key][head] = sum_d K[key][d] q[head][d]: A = 16 keys x 4 dims, B =
+//           4 dims x 16 heads; lane group lg = l/16 walks its quarter of the dims
+//           (a contiguous slice of the key row), one dim per step;
+//   values  O^T[dim][head] += sum_key V[key][dim] P[head][key]: at step j lane group
+//           lg takes key 4*lg + j, whose weight is register j of the lane's score
+//           tile (D[row 4*lg + v][col l%16]), so the weights never move; a lane's
+//           float4 of V at dims 4*(l%16) + 64c .. +3 feeds four tiles, tile (c, comp)
+//           holding dims 64c + 4*row + comp.
+// A workgroup has 4 waves; wave w takes the range's 16-key subtiles w, w + 4, ...
+// with its own online softmax (max and sum per head), and the 4 waves merge through
+// LDS into the record.  q is loaded, normalised and rotated first; only then does
+// each wave request its keys and values (a wave stalls at a load the memory pipeline
+// has no room for, so work queued behind 32 such loads would wait for them).
+constexpr int kMmaKeys = 64;  // keys per workgroup pass: 4 waves x 16
+
 template <int D>
-__global__ __launch_bounds__(1024) void k_attn_part(const float* q, const float* knew,
-                                                    const float* vnew, float* kc, float* vc,
-                                                    float* part, int G, int64_t Tmax, int pos,
-                                                    float theta, int rot_dim, int chunk, int nsplit,
-                                                    AttnQ Q) {
-  constexpr int KS = D + 4;  // padded K row in LDS: lanes reading different rows spread over banks
-  __shared__ __align__(16) float s_k[kTK * KS];
-  __shared__ __align__(16) float s_v[kTK * D];
-  __shared__ __align__(16) float s_q[16 * D];
-  __shared__ float s_cs[2][D / 2];                // cos, sin of the rotation pairs
-  __shared__ __align__(16) float s_kn[D], s_vn[D];  // the token's rotated k and its v
-  __shared__ float s_qr[16], s_kr;                 // RMS scales of the q heads and of k
+__global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* knew,
+                                                  const float* vnew, float* kc, float* vc,
+                                                  float* part, int G, int64_t Tmax, int pos,
+                                                  float theta, int rot_dim, int chunk, int nsplit,
+                                                  AttnQ Q) {
+  constexpr int DQ = D / 4;   // dims per lane group in the score phase
+  constexpr int NC = D / 64;  // 64-dim blocks of the value phase
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) float s_qn[16 * D];  // normalised q rows (rows >= G zero)
+  __shared__ __align__(16) float s_q[16 * D];   // rotated
+  __shared__ float s_cs[2][D / 2];
+  __shared__ __align__(16) float s_kn[D], s_vn[D];
+  __shared__ __align__(16) float s_o[3 * D * 16];  // waves 1..3: value sums [dim][head]
+  __shared__ float s_ml[4][2][16];                // per wave: running max, weight sum per head
   const int g = blockIdx.x, split = blockIdx.y;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = g * G + wv;
-  const int nthr = G * 64;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, lg = lane >> 4;
   const int T = pos + 1;
   const int t0 = split * chunk, t1 = min(T, t0 + chunk);
   const bool owns_pos = t0 <= pos && pos < t1;
   float* kg = kc + (int64_t)g * Tmax * D;
   float* vg = vc + (int64_t)g * Tmax * D;
-  // Tile loads go to registers first, kPF float4 of K and of V per thread: the
-  // range's first tile is requested before the rotation angles and the q rows are
-  // prepared, and each later tile as soon as the one before is in LDS, so HBM
-  // latency overlaps that work and the previous tile's scores.  The loads are
-  // unconditional (row and index clamped into the range: a key past the range or
-  // the row at pos, still stale here, is replaced or ignored when the tile is
-  // stored).  One buffer: the 1024-thread workgroup caps a thread at 128 VGPRs,
-  // and a second buffer spilled across the double-precision angle computation.
-  constexpr int TQ = kTK * D / 4;  // float4 of K (and of V) per tile
-  auto issue = [&](int tb, float4 (&rk)[kPF], float4 (&rv)[kPF]) {
+  const int half = rot_dim / 2;
+
+  // ---- loads, in order of need.  q: the 16 lanes tid = 16*qh + ql of head qh hold its
+  // float4 at dims 64u + 4*ql (u < D/64): coalesced here, and without LDS bank
+  // conflicts below (heads past G read head 0, unused)
+  const int qh = tid >> 4, ql = tid & 15;
+  float4 qv[D / 64], qw[D / 64];
+  {
+    const float* qrow = q + (int64_t)(g * G + (qh < G ? qh : 0)) * Q.q_stride;
+    const float* wrow = Q.qnw ? Q.qnw : q;
 #pragma unroll
-    for (int u = 0; u < kPF; ++u) {
-      const int i = min((int)threadIdx.x + u * nthr, TQ - 1);
-      const int t = min(tb + i / (D / 4), t1 - 1), c4 = i % (D / 4);
-      rk[u] = reinterpret_cast<const float4*>(kg + (int64_t)t * D)[c4];
-      rv[u] = reinterpret_cast<const float4*>(vg + (int64_t)t * D)[c4];
+    for (int u = 0; u < D / 64; ++u) {
+      qv[u] = reinterpret_cast<const float4*>(qrow + 64 * u)[ql];
+      qw[u] = reinterpret_cast<const float4*>(wrow + 64 * u)[ql];
+    }
+  }
+  // the new key and value (every workgroup reads them; the owner of pos uses them):
+  // thread tid < D/4 holds dims 4*tid .. +3
+  float4 kn4 = make_float4(0.f, 0.f, 0.f, 0.f), vn4 = kn4, kw4 = kn4;
+  if (tid < D / 4) {
+    kn4 = reinterpret_cast<const float4*>(knew + (int64_t)g * D)[tid];
+    vn4 = reinterpret_cast<const float4*>(vnew + (int64_t)g * D)[tid];
+    kw4 = reinterpret_cast<const float4*>(Q.knw ? Q.knw : knew)[tid];
+  }
+  // a subtile's loads: K rows in the score operand layout (lane: key r, dims
+  // DQ*lg .. +DQ-1, a contiguous slice) and V rows in the value operand layout (lane:
+  // keys 4*lg + j, dims 4r + 64c ..); keys past the range read its last row
+  float kr[DQ];
+  float4 vr[4][NC];
+  auto load_sub = [&](int kb) {
+    const int key = min(kb + r, t1 - 1);
+    const float4* kp = reinterpret_cast<const float4*>(kg + (int64_t)key * D + DQ * lg);
+#pragma unroll
+    for (int u = 0; u < DQ / 4; ++u) {
+      const float4 f = kp[u];
+      kr[4 * u] = f.x, kr[4 * u + 1] = f.y, kr[4 * u + 2] = f.z, kr[4 * u + 3] = f.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vk = min(kb + 4 * lg + j, t1 - 1);
+      const float4* vp = reinterpret_cast<const float4*>(vg + (int64_t)vk * D) + r;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vr[j][c] = vp[16 * c];
     }
   };
-  float4 rk[kPF], rv[kPF];
-  issue(t0, rk, rv);
-  const int half = rot_dim / 2;
-  for (int i = threadIdx.x; i < half; i += nthr) {
-    // in double: pos * theta^(-2i/rot_dim) reaches 1e4 rad and more
-    const double ang = (double)pos * pow((double)theta, -2.0 * i / rot_dim);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    s_cs[0][i] = (float)cs;
-    s_cs[1][i] = (float)sn;
+  // ---- rotation angles.  pos * theta^(-2i/rot_dim) reaches 1e4 rad and more, so the
+  // angle is formed and reduced modulo 2 pi in double (2 pi in two parts: exact for
+  // these magnitudes); the cosine and sine of the reduced angle are taken in float
+  static_assert(D / 2 <= 256, "one thread per rotation pair");
+  if (tid < half) {
+    const double f = exp(-2.0 * tid / rot_dim * log((double)theta));
+    const double ang = (double)pos * f;
+    const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+    const double red = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, ang));
+    float sn, cs;
+    sincosf((float)red, &sn, &cs);
+    s_cs[0][tid] = cs;
+    s_cs[1][tid] = sn;
   }
-  // RMS normalisation scales, 1 / sqrt(mean(x^2) + eps): wave wv for query head
-  // h = g*G + wv, wave 0 of the workgroup that owns pos for the new key
-  auto rms_scale = [&](const float* x) -> float {
-    float ss = 0.f;
+  // ---- q normalisation: 1 / sqrt(mean(x^2) + eps) over the head's D dims (its 16
+  // lanes add their sums); the result goes to s_qn and, for the dims past rot_dim
+  // (the pair pass below overwrites the others), to s_q
+  {
+    float rq = 1.f;
+    if (Q.qnw) {
+      float ss = 0.f;
 #pragma unroll
-    for (int d = lane; d < D; d += 64) ss = fmaf(x[d], x[d], ss);
+      for (int u = 0; u < D / 64; ++u)
+        ss = fmaf(qv[u].x, qv[u].x, fmaf(qv[u].y, qv[u].y, fmaf(qv[u].z, qv[u].z, fmaf(qv[u].w, qv[u].w, ss))));
+#pragma unroll
+      for (int o2 = 1; o2 < 16; o2 <<= 1) ss += __shfl_xor(ss, o2);
+      rq = 1.0f / sqrtf(ss / (float)D + Q.eps);
+    }
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) {
+      float4 x = qv[u];
+      if (Q.qnw) x = make_float4(x.x * rq * qw[u].x, x.y * rq * qw[u].y, x.z * rq * qw[u].z, x.w * rq * qw[u].w);
+      if (qh >= G) x = make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4*>(s_qn + qh * D + 64 * u)[ql] = x;
+      reinterpret_cast<float4*>(s_q + qh * D + 64 * u)[ql] = x;
+    }
+  }
+  // the new key's normalisation (threads below D/4 hold it: one wave, or part of one)
+  float kn[4] = {kn4.x, kn4.y, kn4.z, kn4.w};
+  if (Q.knw && owns_pos && wv == 0) {
+    float ss = fmaf(kn4.x, kn4.x, fmaf(kn4.y, kn4.y, fmaf(kn4.z, kn4.z, kn4.w * kn4.w)));
+    if (tid >= D / 4) ss = 0.f;
 #pragma unroll
     for (int o2 = 32; o2 >= 1; o2 >>= 1) ss += __shfl_xor(ss, o2);
-    return 1.0f / sqrtf(ss / (float)D + Q.eps);
-  };
-  if (Q.qnw) {
-    const float r = rms_scale(q + (int64_t)h * Q.q_stride);
-    if (lane == 0) s_qr[wv] = r;
+    const float rk = 1.0f / sqrtf(ss / (float)D + Q.eps);
+    kn[0] *= rk * kw4.x, kn[1] *= rk * kw4.y, kn[2] *= rk * kw4.z, kn[3] *= rk * kw4.w;
   }
-  if (Q.knw && owns_pos && wv == 0) {
-    const float r = rms_scale(knew + (int64_t)g * D);
-    if (lane == 0) s_kr = r;
+  if (owns_pos && tid < D / 4) {
+    reinterpret_cast<float4*>(s_kn)[tid] = make_float4(kn[0], kn[1], kn[2], kn[3]);  // rotated below
+    reinterpret_cast<float4*>(s_vn)[tid] = vn4;
   }
-  if (Q.gate && split == 0)  // the gate halves of the group's query rows, copied out
-    for (int i = threadIdx.x; i < G * D; i += nthr)
-      Q.gate[(int64_t)(g * G + i / D) * D + i % D] = q[(int64_t)(g * G + i / D) * Q.q_stride + D + i % D];
   __syncthreads();
-  // x_d of a row, scaled by r * w_d (normalised) when w is given, then rotated:
-  // pair (d, d + half) for d < half, (d - half, d) below rot_dim
-  auto rot = [&](const float* x, int d, float r, const float* w) -> float {
-    auto val = [&](int e) { return w ? x[e] * r * w[e] : x[e]; };
-    if (d < half) return val(d) * s_cs[0][d] - val(d + half) * s_cs[1][d];
-    if (d < rot_dim) return val(d) * s_cs[0][d - half] + val(d - half) * s_cs[1][d - half];
-    return val(d);
-  };
-  for (int i = threadIdx.x; i < G * D; i += nthr)
-    s_q[i] = rot(q + (int64_t)(g * G + i / D) * Q.q_stride, i % D, Q.qnw ? s_qr[i / D] : 1.f, Q.qnw);
-  if (owns_pos) {
-    for (int d = threadIdx.x; d < D; d += nthr) {
-      const float kr = rot(knew + (int64_t)g * D, d, Q.knw ? s_kr : 1.f, Q.knw),
-                  vr = vnew[(int64_t)g * D + d];
-      s_kn[d] = kr;
-      s_vn[d] = vr;
-      kg[(int64_t)pos * D + d] = kr;
-      vg[(int64_t)pos * D + d] = vr;
+  // ---- rotations by pairs: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s, x_{i+half} c +
+  // x_i s) for i < half, consecutive pairs on consecutive lanes; the new key's pairs
+  // (its row is one more item list) after the 16 q rows
+  float kpair[2][2];  // the key pair of this thread, if any (half <= 128 < 256: at most one)
+  for (int it = tid; it < 17 * half; it += 256) {
+    const int hh = it / half, i = it % half;
+    const float* src = hh < 16 ? s_qn + hh * D : s_kn;
+    const float x1 = src[i], x2 = src[i + half], c = s_cs[0][i], sn = s_cs[1][i];
+    const float y1 = fmaf(x1, c, -x2 * sn), y2 = fmaf(x2, c, x1 * sn);
+    if (hh < 16) {
+      s_q[hh * D + i] = y1;
+      s_q[hh * D + i + half] = y2;
+    } else {
+      kpair[(it - tid) / 256 & 1][0] = y1;
+      kpair[(it - tid) / 256 & 1][1] = y2;
     }
   }
-  const float scale = 1.0f / sqrtf((float)D);
-  float m = -INFINITY, l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int kt = lane % kTK, kh = lane / kTK;  // score phase: key kt, part kh of the dims
-  for (int tb = t0; tb < t1; tb += kTK) {
-    const int nk = min(kTK, t1 - tb);
-    __syncthreads();  // the previous tile is consumed (and s_q, s_kn, s_vn are written)
-    // the tile from its registers into LDS (slots past the registers' reach, when
-    // the workgroup has fewer than TQ / kPF threads, are loaded here directly)
-    auto put = [&](int i, float4 kv, float4 vv) {
-      const int t = i / (D / 4), c4 = i % (D / 4);
-      if (tb + t == pos) {  // this token: from LDS (its cache row is written above)
-        kv = reinterpret_cast<const float4*>(s_kn)[c4];
-        vv = reinterpret_cast<const float4*>(s_vn)[c4];
+  __syncthreads();  // s_kn is read above and rewritten below
+  if (owns_pos) {
+    for (int it = tid; it < 17 * half; it += 256)
+      if (it >= 16 * half) {
+        const int i = it - 16 * half;
+        s_kn[i] = kpair[(it - tid) / 256 & 1][0];
+        s_kn[i + half] = kpair[(it - tid) / 256 & 1][1];
       }
-      *reinterpret_cast<float4*>(s_k + t * KS + 4 * c4) = kv;
-      reinterpret_cast<float4*>(s_v)[i] = vv;
-    };
+  }
+  __syncthreads();
+  if (owns_pos && tid < D / 4) {  // the rotated key and the value into row pos of the caches
+    reinterpret_cast<float4*>(kg + (int64_t)pos * D)[tid] = reinterpret_cast<const float4*>(s_kn)[tid];
+    reinterpret_cast<float4*>(vg + (int64_t)pos * D)[tid] = vn4;
+  }
+  // the wave's first keys and values, requested only now: a wave cannot issue past
+  // a load the memory pipeline has no room for, and the work above would wait
+  // behind them
+  const int kb0 = t0 + 16 * wv;
+  load_sub(min(kb0, t1 - 1));  // a wave with no subtile loads the last row, unused
+  const float scale = 1.0f / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f;  // of head r (every lane group holds the same)
+  f32x4 o[NC][4];
 #pragma unroll
-    for (int u = 0; u < kPF; ++u) {
-      const int i = (int)threadIdx.x + u * nthr;
-      if (i < TQ) put(i, rk[u], rv[u]);
-    }
-    for (int i = (int)threadIdx.x + kPF * nthr; i < TQ; i += nthr) {
-      const int t = min(tb + i / (D / 4), t1 - 1), c4 = i % (D / 4);
-      put(i, reinterpret_cast<const float4*>(kg + (int64_t)t * D)[c4],
-          reinterpret_cast<const float4*>(vg + (int64_t)t * D)[c4]);
-    }
-    __syncthreads();
-    if (tb + kTK < t1) issue(tb + kTK, rk, rv);  // the next tile, into the freed registers
-    // scores: lane (kt, kh) sums part kh of q_h . K_kt
-    float sp = 0.f;
-    const float* kr = s_k + kt * KS + kh * (D / kSPL);
-    const float* qh = s_q + wv * D + kh * (D / kSPL);
-#pragma unroll 8
-    for (int c = 0; c < D / kSPL; c += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(kr + c);
-      const float4 b = *reinterpret_cast<const float4*>(qh + c);
-      sp = fmaf(a.x, b.x, sp);
-      sp = fmaf(a.y, b.y, sp);
-      sp = fmaf(a.z, b.z, sp);
-      sp = fmaf(a.w, b.w, sp);
-    }
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int o = 32; o >= kTK; o >>= 1) sp += __shfl_xor(sp, o);
-    const float sc = kt < nk ? sp * scale : -INFINITY;
-    float tmax = sc;
+    for (int cp = 0; cp < 4; ++cp) o[c][cp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = kb0; kb < t1; kb += 4 * 16) {
+    if (kb != kb0) load_sub(kb);
+    // the row at pos (also where a key past the range was clamped to it) was read
+    // before this call wrote it: the new key and value instead
+    if (owns_pos && min(kb + r, t1 - 1) == pos) {
 #pragma unroll
-    for (int o = kTK / 2; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+      for (int s2 = 0; s2 < DQ; ++s2) kr[s2] = s_kn[DQ * lg + s2];
+    }
+    if (owns_pos) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (min(kb + 4 * lg + j, t1 - 1) == pos) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) vr[j][c] = reinterpret_cast<const float4*>(s_vn)[r + 16 * c];
+        }
+    }
+    // scores of the subtile's 16 keys for the 16 heads (q from LDS, 16 dims at a time)
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h4 = 0; h4 < DQ / 16; ++h4) {
+      float qa[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 e = reinterpret_cast<const float4*>(s_q + r * D + DQ * lg + 16 * h4)[u];
+        qa[4 * u] = e.x, qa[4 * u + 1] = e.y, qa[4 * u + 2] = e.z, qa[4 * u + 3] = e.w;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) st = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[16 * h4 + s2], qa[s2], st, 0, 0, 0);
+    }
+    // lane: keys kb + 4*lg + v of head r
+    const int nk = min(16, t1 - kb);
+    float sv[4], tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = 4 * lg + v < nk ? st[v] * scale : -INFINITY;
+      tmax = fmaxf(tmax, sv[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mn = fmaxf(m, tmax);
-    const float corr = __expf(m - mn);  // m = -inf on the first tile: 0
-    const float p = kt < nk ? __expf(sc - mn) : 0.f;
-    float ps = p;
+    const float corr = __expf(m - mn);  // m = -inf on the first subtile: 0
+    float p[4], ps = 0.f;
 #pragma unroll
-    for (int o = kTK / 2; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
+    for (int v = 0; v < 4; ++v) {
+      p[v] = 4 * lg + v < nk ? __expf(sv[v] - mn) : 0.f;
+      ps += p[v];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
     l = fmaf(l, corr, ps);
     m = mn;
-    acc.x *= corr;
-    acc.y *= corr;
-    acc.z *= corr;
-    acc.w *= corr;
-    // values: lane owns dims 4*lane .. 4*lane+3 (a lane past D/4 repeats lane 0's
-    // dims and stores nothing); the weight of key t comes from lane t
-    const int vl = lane < D / 4 ? lane : 0;
-    for (int t = 0; t < nk; ++t) {
-      const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t));
-      const float4 vv = reinterpret_cast<const float4*>(s_v + t * D)[vl];
-      acc.x = fmaf(pt, vv.x, acc.x);
-      acc.y = fmaf(pt, vv.y, acc.y);
-      acc.z = fmaf(pt, vv.z, acc.z);
-      acc.w = fmaf(pt, vv.w, acc.w);
+    // values: the tiles' columns are heads, so the rescale is the lane's own corr
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int cp = 0; cp < 4; ++cp) o[c][cp] *= corr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        o[c][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[j][c].x, p[j], o[c][0], 0, 0, 0);
+        o[c][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[j][c].y, p[j], o[c][1], 0, 0, 0);
+        o[c][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[j][c].z, p[j], o[c][2], 0, 0, 0);
+        o[c][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[j][c].w, p[j], o[c][3], 0, 0, 0);
+      }
+  }
+  // ---- the 4 waves' states merged: M = max m_w, O = sum_w e^(m_w - M) O_w, L likewise.
+  // Tile (c, cp) register v of lane l: dim 64c + 4*(4*lg + v) + cp, head r.
+  if (lg == 0) {
+    s_ml[wv][0][r] = m;
+    s_ml[wv][1][r] = l;
+  }
+  __syncthreads();
+  if (wv > 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int cp = 0; cp < 4; ++cp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_o[(wv - 1) * D * 16 + (64 * c + 4 * (4 * lg + v) + cp) * 16 + r] = o[c][cp][v];
+  }
+  __syncthreads();
+  if (wv == 0) {
+    float M = s_ml[0][0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[w][0][r]);
+    float f[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_ml[w][0][r];
+      f[w] = mw == -INFINITY ? 0.f : __expf(mw - M);  // a wave with no keys weighs 0
+      L = fmaf(f[w], s_ml[w][1][r], L);
+    }
+    if (r < G) {
+      float* out = part + ((int64_t)(g * G + r) * nsplit + split) * rec<D>();
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int cp = 0; cp < 4; ++cp)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int d = 64 * c + 4 * (4 * lg + v) + cp;
+            float a = f[0] * o[c][cp][v];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) a = fmaf(f[w], s_o[(w - 1) * D * 16 + d * 16 + r], a);
+            out[d] = a;
+          }
+      if (lg == 0) {
+        out[D] = M;
+        out[D + 1] = L;
+      }
     }
   }
-  float* out = part + ((int64_t)h * nsplit + split) * rec<D>();
-  if (lane < D / 4) reinterpret_cast<float4*>(out)[lane] = acc;
-  if (lane == 0) {
-    out[D] = m;
-    out[D + 1] = l;
-  }
+  if (Q.gate && split == 0)  // the gate halves of the group's query rows, copied out
+    for (int i = tid; i < G * D; i += 256)
+      Q.gate[(int64_t)(g * G + i / D) * D + i % D] = q[(int64_t)(g * G + i / D) * Q.q_stride + D + i % D];
 }
 
 // The partial results of head h merged: weights w_s = exp(m_s - M) of the splits,
@@ -288,15 +401,13 @@ __global__ __launch_bounds__(1024) void k_attn_combine(const float* part, float*
   }
 }
 
-// keys per split: about one workgroup per CU (a workgroup fills a CU's LDS), whole
-// tiles
-// (128 ranges measured 35.7 us)
-constexpr int kWantSplits = 256;  // 512 measured slower (30.2 us)
-int attn_chunk(int Hkv, int T) {
+// key ranges: about one workgroup per CU, in whole passes of the 4 waves
+constexpr int kWantSplits = 256;
+int attn_chunk(int Hkv, int T, int unit) {
   const int64_t want = kWantSplits;
   int64_t c = ((int64_t)T * Hkv + want - 1) / want;
-  c = (c + kTK - 1) / kTK * kTK;
-  return (int)(c < kTK ? kTK : c);
+  c = (c + unit - 1) / unit * unit;
+  return (int)(c < unit ? unit : c);
 }
 
 template <int D>
@@ -304,11 +415,11 @@ hipError_t launch_d(const float* q, const float* k, const float* v, float* kc, f
                     int Hkv, int64_t Tmax, int pos, float theta, int rot_dim, float* o, float* ws,
                     const AttnQ& Q, hipStream_t s) {
   const int T = pos + 1, G = Hq / Hkv;
-  const int chunk = attn_chunk(Hkv, T);
-  const int nsplit = (T + chunk - 1) / chunk;
   float* part = ws;
-  hipLaunchKernelGGL(k_attn_part<D>, dim3(Hkv, nsplit), dim3(G * 64), 0, s, q, k, v, kc, vc, part, G,
-                     Tmax, pos, theta, rot_dim, chunk, nsplit, Q);
+  const int chunk = attn_chunk(Hkv, T, kMmaKeys);
+  const int nsplit = (T + chunk - 1) / chunk;
+  hipLaunchKernelGGL(k_attn_mma<D>, dim3(Hkv, nsplit), dim3(256), 0, s, q, k, v, kc, vc, part, G, Tmax,
+                     pos, theta, rot_dim, chunk, nsplit, Q);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_attn_combine<D>, dim3(Hq), dim3(1024), 0, s, part, o, nsplit);
@@ -317,10 +428,10 @@ hipError_t launch_d(const float* q, const float* k, const float* v, float* kc, f
 
 }  // namespace
 
-// splits of any T <= Tmax: at most ceil(T / kTK) (chunks hold whole tiles) and at most
-// ceil(256 / Hkv) (chunks hold at least T * Hkv / 256 keys)
+// ranges of any T <= Tmax: at most ceil(T / kMmaKeys) (ranges hold whole passes) and
+// at most ceil(256 / Hkv) (ranges hold at least T * Hkv / 256 keys)
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int Tmax) {
-  const int64_t a = ((int64_t)Tmax + kTK - 1) / kTK, b = (kWantSplits + Hkv - 1) / Hkv;
+  const int64_t a = ((int64_t)Tmax + kMmaKeys - 1) / kMmaKeys, b = (kWantSplits + Hkv - 1) / Hkv;
   const int64_t nsplit = a < b ? a : b;
   return (size_t)((int64_t)Hq * nsplit * (D + 4)) * 4;
 }
