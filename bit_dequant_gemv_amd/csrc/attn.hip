@@ -55,9 +55,8 @@ struct AttnQ {
 //           holding dims 64c + 4*row + comp.
 // A workgroup has 4 waves; wave w takes the range's 16-key subtiles w, w + 4, ...
 // with its own online softmax (max and sum per head), and the 4 waves merge through
-// LDS into the record.  q is loaded, normalised and rotated first; only then does
-// each wave request its keys and values (a wave stalls at a load the memory pipeline
-// has no room for, so work queued behind 32 such loads would wait for them).
+// LDS into the record.  Each wave requests its keys, then q is normalised and rotated,
+// then the wave requests its values.
 constexpr int kMmaKeys = 64;  // keys per workgroup pass: 4 waves x 16
 
 template <int D>
@@ -69,11 +68,14 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
   constexpr int DQ = D / 4;   // dims per lane group in the score phase
   constexpr int NC = D / 64;  // 64-dim blocks of the value phase
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ __align__(16) float s_qn[16 * D];  // normalised q rows (rows >= G zero)
-  __shared__ __align__(16) float s_q[16 * D];   // rotated
+  // normalised q rows (rows >= G zero), then rotated; after the key loop the same
+  // memory holds two waves' value sums [dim][head] for the merge
+  __shared__ __align__(16) float s_qq[2 * 16 * D];
+  float* s_qn = s_qq;
+  float* s_q = s_qq + 16 * D;
+  float* s_o = s_qq;
   __shared__ float s_cs[2][D / 2];
   __shared__ __align__(16) float s_kn[D], s_vn[D];
-  __shared__ __align__(16) float s_o[3 * D * 16];  // waves 1..3: value sums [dim][head]
   __shared__ float s_ml[4][2][16];                // per wave: running max, weight sum per head
   const int g = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
   // keys 4*lg + j, dims 4r + 64c ..); keys past the range read its last row
   float kr[DQ];
   float4 vr[4][NC];
-  auto load_sub = [&](int kb) {
+  auto load_k = [&](int kb) {
     const int key = min(kb + r, t1 - 1);
     const float4* kp = reinterpret_cast<const float4*>(kg + (int64_t)key * D + DQ * lg);
 #pragma unroll
@@ -120,6 +122,8 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
       const float4 f = kp[u];
       kr[4 * u] = f.x, kr[4 * u + 1] = f.y, kr[4 * u + 2] = f.z, kr[4 * u + 3] = f.w;
     }
+  };
+  auto load_v = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int vk = min(kb + 4 * lg + j, t1 - 1);
@@ -128,6 +132,12 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
       for (int c = 0; c < NC; ++c) vr[j][c] = vp[16 * c];
     }
   };
+  auto load_sub = [&](int kb) { load_k(kb); load_v(kb); };
+  const int kb0 = t0 + 16 * wv;
+  // the keys go out before the prologue, the values after it: the prologue's work is
+  // not queued behind all 32 loads (a wave stalls at a load the memory pipeline has no
+  // room for), and the scores, which need the keys first, start sooner
+  load_k(min(kb0, t1 - 1));  // a wave with no subtile loads the last row, unused
   // ---- rotation angles.  pos * theta^(-2i/rot_dim) reaches 1e4 rad and more, so the
   // angle is formed and reduced modulo 2 pi in double (2 pi in two parts: exact for
   // these magnitudes); the cosine and sine of the reduced angle are taken in float
@@ -211,11 +221,7 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
     reinterpret_cast<float4*>(kg + (int64_t)pos * D)[tid] = reinterpret_cast<const float4*>(s_kn)[tid];
     reinterpret_cast<float4*>(vg + (int64_t)pos * D)[tid] = vn4;
   }
-  // the wave's first keys and values, requested only now: a wave cannot issue past
-  // a load the memory pipeline has no room for, and the work above would wait
-  // behind them
-  const int kb0 = t0 + 16 * wv;
-  load_sub(min(kb0, t1 - 1));  // a wave with no subtile loads the last row, unused
+  load_v(min(kb0, t1 - 1));
   const float scale = 1.0f / sqrtf((float)D);
   float m = -INFINITY, l = 0.f;  // of head r (every lane group holds the same)
   f32x4 o[NC][4];
@@ -289,32 +295,53 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
         o[c][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[j][c].w, p[j], o[c][3], 0, 0, 0);
       }
   }
-  // ---- the 4 waves' states merged: M = max m_w, O = sum_w e^(m_w - M) O_w, L likewise.
+  // ---- the 4 waves' states merged: M = max m_w, O = sum_w e^(m_w - M) O_w, L likewise,
+  // in two rounds through the q buffers (free once every wave is past its loop): waves
+  // 2, 3 hand their weighted sums to waves 0, 1, then wave 1 to wave 0.
   // Tile (c, cp) register v of lane l: dim 64c + 4*(4*lg + v) + cp, head r.
   if (lg == 0) {
     s_ml[wv][0][r] = m;
     s_ml[wv][1][r] = l;
   }
   __syncthreads();
-  if (wv > 0) {
+  float M = s_ml[0][0][r];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[w][0][r]);
+  const float fw = m == -INFINITY ? 0.f : __expf(m - M);  // this wave's weight (no keys: 0)
+  auto put_o = [&](int slot) {  // the wave's sums, already weighted
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int cp = 0; cp < 4; ++cp)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s_o[(wv - 1) * D * 16 + (64 * c + 4 * (4 * lg + v) + cp) * 16 + r] = o[c][cp][v];
-  }
+        for (int v = 0; v < 4; ++v)
+          s_o[slot * D * 16 + (64 * c + 4 * (4 * lg + v) + cp) * 16 + r] = o[c][cp][v];
+  };
+  auto add_o = [&](int slot) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int cp = 0; cp < 4; ++cp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[c][cp][v] += s_o[slot * D * 16 + (64 * c + 4 * (4 * lg + v) + cp) * 16 + r];
+  };
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int cp = 0; cp < 4; ++cp) o[c][cp] *= fw;
+  if (wv >= 2) put_o(wv - 2);
+  __syncthreads();
+  if (wv < 2) add_o(wv);
+  __syncthreads();
+  if (wv == 1) put_o(0);
   __syncthreads();
   if (wv == 0) {
-    float M = s_ml[0][0][r];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[w][0][r]);
-    float f[4], L = 0.f;
+    add_o(0);
+    float L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = s_ml[w][0][r];
-      f[w] = mw == -INFINITY ? 0.f : __expf(mw - M);  // a wave with no keys weighs 0
-      L = fmaf(f[w], s_ml[w][1][r], L);
+      L = fmaf(mw == -INFINITY ? 0.f : __expf(mw - M), s_ml[w][1][r], L);
     }
     if (r < G) {
       float* out = part + ((int64_t)(g * G + r) * nsplit + split) * rec<D>();
@@ -323,13 +350,7 @@ __global__ __launch_bounds__(256) void k_attn_mma(const float* q, const float* k
 #pragma unroll
         for (int cp = 0; cp < 4; ++cp)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int d = 64 * c + 4 * (4 * lg + v) + cp;
-            float a = f[0] * o[c][cp][v];
-#pragma unroll
-            for (int w = 1; w < 4; ++w) a = fmaf(f[w], s_o[(w - 1) * D * 16 + d * 16 + r], a);
-            out[d] = a;
-          }
+          for (int v = 0; v < 4; ++v) out[64 * c + 4 * (4 * lg + v) + cp] = o[c][cp][v];
       if (lg == 0) {
         out[D] = M;
         out[D + 1] = L;
