@@ -377,7 +377,12 @@ def test_layer_call_counter_wraps(q):
 @pytest.mark.parametrize("E,H,I,bits,K,T", [(64, 1024, 256, 4, 4, 16), (512, 4096, 1024, 4, 4, 64),
                                             (512, 4096, 1024, 2, 4, 8), (8, 256, 128, 4, 8, 5),
                                             # every expert gets 40 pairs: chunks of 32 and 8
-                                            (4, 256, 128, 4, 4, 40)])
+                                            (4, 256, 128, 4, 4, 40),
+                                            # other row-block shapes of the shared expert's
+                                            # matrix-core chunks: 16 lanes per row and 3 blocks
+                                            # of 64 rows; a block of 256 rows over I = 64 (its
+                                            # last 12 tiles empty); ragged token chunks
+                                            (16, 512, 192, 4, 4, 20), (8, 256, 64, 2, 2, 37)])
 def test_batched_parity(q, E, H, I, bits, K, T):
     say("batched", E, H, I, bits, K, T)
     D = DeviceLayer(1004 if E == 512 else 5000 + E, 0, E, H, I, bits, K)
