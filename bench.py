@@ -668,9 +668,10 @@ def run_batched_bench(args, torch, q, synth):
             "cfg": {"batch": T}}
 
 
-PHASES = ["start", "x in LDS", "router dots done, shared rows issued", "x planes", "shared gate/up dots",
-          "logits polled", "top-K ranked", "routed rows issued", "routed gate/up done (wave 0)",
-          "all flags seen", "h in LDS", "h planes", "down rows", "end"]
+PHASES = ["start", "x in LDS", "router dots done", "x planes in LDS", "x planes in registers",
+          "logits polled", "top-K ranked", "shared and routed rows issued",
+          "shared + routed gate/up done (wave 0)", "all flags seen", "h in LDS", "h planes", "down rows",
+          "end"]
 
 
 def run_phase_probe(args, torch, q, synth):

@@ -364,8 +364,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   uint32_t ssp[2][CPLH];
   uint4 dq[1 + MAXR];
   uint32_t dsc[1 + MAXR];
-  // a stack issues them here for its first layer and, for each later layer, during
-  // the tail of the one before (see the end of step 8)
+  // (issued in step 5, in every layer, once the workgroup's logits have arrived)
   // the next layer's loads (stack only)
   uint4 gqN, rqN[CPLR];
   float nwN[8];
@@ -441,11 +440,6 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     router_fetch(Lp.router, r0 + (wv >> 2), rq);
     router_rows(r0);
   }
-  // a single layer issues the shared expert's loads only now: in step 1 they would
-  // share the start-up burst with the router rows, whose logits everything else
-  // waits for (the down item in registers: HBM would otherwise idle during the
-  // top-K)
-  shared_fetch(Lp.sblk, qsp, ssp, dq[0], dsc[0]);
   QMOE_PT(2);
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
@@ -462,8 +456,8 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   uint64_t* hs = Lp.hs + (size_t)(tag % kSlotsH) * I;
   uint64_t* hr = Lp.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
   // the first poll of logits 0..kLB-1 (step 5) goes out now, unconditionally (a
-  // lane past E reads logit E - 1), so that its round trip overlaps the shared
-  // gate/up dots; logits from kLB on are first read by the poll loop of step 5
+  // lane past E reads logit E - 1), so that its round trip overlaps the loading of
+  // the x planes; logits from kLB on are first read by the poll loop of step 5
   uint64_t lraw[PER_L];
   uint32_t pending = 0;
   {
@@ -477,17 +471,6 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   }
   dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
   float hs_val = 0.f;
-  // ---- 4. shared gate/up + SwiGLU -> hs (one item per wave at most; the logits
-  //         of the other workgroups are still on their way meanwhile; hs is stored
-  //         after the top-K)
-  if (has_sp) {
-    float p[2];
-    dH.template dots<2>(qsp, ssp, p);
-    const float a = group_sum_last<LGH>(p[0]);
-    const float u = group_sum_last<LGH>(p[1]);
-    hs_val = silu_f(a) * u;
-  }
-
   QMOE_PT(4);
   // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the
   //         logits' bits mapped to an order-preserving u32 (-0 counts as +0).
@@ -531,6 +514,12 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     if (lane == 0) s_wmax[wv] = wmax;
     __syncthreads();
   QMOE_PT(5);
+    // the shared expert's rows (and its down item) go out only now, once this
+    // workgroup's logits have all arrived: issued with the router rows or right
+    // after them, their 7 MB flood the memory system while the logit stores of the
+    // slowest workgroups are still becoming visible, and the poll above ends ~0.3 us
+    // later (measured); here they travel during the ranking, ahead of the routed rows
+    shared_fetch(Lp.sblk, qsp, ssp, dq[0], dsc[0]);
     uint32_t L;
     {
       const uint32_t mi = lane < kLW ? s_wmax[lane] : 0u;
@@ -601,7 +590,6 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
         Lp.w_out[k] = wsel[k];
       }
   }
-  if (has_sp && group_last<LGH>(lane)) tag_put(hs + jsp, hs_val, tag);
 
   // ---- 6. loads: two routed gate/up row pairs per wave
   const int n_rp = K * NSP;
@@ -658,6 +646,16 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
                             (uint32_t)(subi * GI + gli / QTraits<BITS>::CPG));
   }
   QMOE_PT(7);
+  // ---- 4. shared gate/up + SwiGLU -> hs (one item per wave at most): computed
+  //         only here, while the routed rows of step 6 travel
+  if (has_sp) {
+    float p[2];
+    dH.template dots<2>(qsp, ssp, p);
+    const float a = group_sum_last<LGH>(p[0]);
+    const float u = group_sum_last<LGH>(p[1]);
+    hs_val = silu_f(a) * u;
+    if (group_last<LGH>(lane)) tag_put(hs + jsp, hs_val, tag);
+  }
   // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step (the first
   //         step outside the loop, so that its dots wait for their own rows only,
   //         not for the down rows issued after them)
