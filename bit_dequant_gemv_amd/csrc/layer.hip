@@ -340,20 +340,22 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
 
   const float resid_v = A.residual[row0 + min((int)tx, kRB - 1)];
   float resid = (int)tx < kRB ? resid_v : 0.f;
-  // the shared expert's loads: one gate/up row pair per rank below I/RPWH and the
-  // wave's shared down item (waves below DITEMS; another wave reads rows it
-  // ignores), into registers
+  // the shared expert's loads, into registers: one gate/up row pair per rank below
+  // I/RPWH (another wave reads rows of item 0 that it ignores) ...
   const bool has_sp = rank < NSP;
   int jsp = rank * RPWH + subh;
   int nl_s = wv * RPWI + subi;
   RowDot<BITS, LGH, CPLH> dH;
-  auto shared_fetch = [&](const uint8_t* sblk, uint4(&qd)[2][CPLH], uint32_t(&sd)[2][CPLH],
-                          uint4& d0, uint32_t& s0) {
+  auto shared_fetch = [&](const uint8_t* sblk, uint4(&qd)[2][CPLH], uint32_t(&sd)[2][CPLH]) {
     const int j = has_sp ? jsp : subh;  // no item: rows of item 0, ignored
     const uint8_t* cr[2] = {sblk + A.off_g + j * RBH, sblk + A.off_u + j * RBH};
     const uint32_t* sr[2] = {reinterpret_cast<const uint32_t*>(sblk + A.off_gsb) + j * GH,
                              reinterpret_cast<const uint32_t*>(sblk + A.off_usb) + j * GH};
     dH.template fetch_always<2>(cr, sr, glh, qd, sd);
+  };
+  // ... and the wave's shared down item (waves below DITEMS; another wave reads
+  // rows it ignores)
+  auto shared_down_fetch = [&](const uint8_t* sblk, uint4& d0, uint32_t& s0) {
     // a wave-uniform row base plus a 32-bit lane offset
     const int rb = wv < DITEMS ? row0 + wv * RPWI : row0;
     d0 = ld_stream16(sblk + A.off_d + (int64_t)rb * RBI + (uint32_t)(subi * RBI + 16 * gli));
@@ -364,7 +366,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   uint32_t ssp[2][CPLH];
   uint4 dq[1 + MAXR];
   uint32_t dsc[1 + MAXR];
-  // (issued in step 5, in every layer, once the workgroup's logits have arrived)
+  // (the down item is issued in step 2, the gate/up pair in step 5)
   // the next layer's loads (stack only)
   uint4 gqN, rqN[CPLR];
   float nwN[8];
@@ -441,6 +443,13 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     router_rows(r0);
   }
   QMOE_PT(2);
+  // the shared down item goes out now, behind the logit stores: 2 MB that would
+  // otherwise join the stream after the top-K, small enough not to hold up the
+  // logits' visibility (measured against issuing it in step 5: 15.27 against 15.72
+  // us per layer, 2-bit 14.74 against 14.92; in step 1, before the router dots or
+  // after the first logit poll it gains less, and the shared gate rows issued here
+  // as well lose part of the gain)
+  shared_down_fetch(Lp.sblk, dq[0], dsc[0]);
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
   prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
@@ -514,12 +523,12 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     if (lane == 0) s_wmax[wv] = wmax;
     __syncthreads();
   QMOE_PT(5);
-    // the shared expert's rows (and its down item) go out only now, once this
-    // workgroup's logits have all arrived: issued with the router rows or right
-    // after them, their 7 MB flood the memory system while the logit stores of the
-    // slowest workgroups are still becoming visible, and the poll above ends ~0.3 us
-    // later (measured); here they travel during the ranking, ahead of the routed rows
-    shared_fetch(Lp.sblk, qsp, ssp, dq[0], dsc[0]);
+    // the shared expert's gate/up rows go out only now, once this workgroup's
+    // logits have all arrived: issued with the router rows or right after them,
+    // they flood the memory system while the logit stores of the slowest
+    // workgroups are still becoming visible, and the poll above ends later
+    // (measured); here they travel during the ranking, ahead of the routed rows
+    shared_fetch(Lp.sblk, qsp, ssp);
     uint32_t L;
     {
       const uint32_t mi = lane < kLW ? s_wmax[lane] : 0u;
@@ -703,7 +712,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   if (wg == 0 && tx == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
-      hr, K * I, s_h, hs, I, s_h + kFusedMaxK * I, tag, ok_all);
+      hr, K * I, s_h, hs, I, s_h + K * I, tag, ok_all);
   __syncthreads();
   QMOE_PT(10);
   if constexpr (STACK) {
@@ -723,9 +732,10 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       router_fetch(rtN, wg * 2 + (wv >> 2), rqN);
     }
   }
-  // fixed-point planes of the h vectors, one pass over s_h (a chunk never straddles
-  // two vectors; unused routed slots hold stale values whose planes are not read)
-  prep_x_coop<BITS>(s_h, (kFusedMaxK + 1) * I, s_hp, s_hsc, s_hsum, tx, kLB);
+  // fixed-point planes of the K + 1 h vectors, one pass over s_h (a chunk never
+  // straddles two vectors).  Only the vectors in use: with K = 4 of 8 slots, the
+  // pass over all slots cost five instead of three wave passes per SIMD.
+  prep_x_coop<BITS>(s_h, (K + 1) * I, s_hp, s_hsc, s_hsum, tx, kLB);
   __syncthreads();
   QMOE_PT(11);
   // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
@@ -740,8 +750,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   if (wv < DITEMS || kw < K) {
     const int kr = kw < kFusedMaxK ? kw : kFusedMaxK;
     RowDot<BITS, LGI, 1> dS, dR;
-    dS.load_prepped(s_hp + kFusedMaxK * CI * PW, s_hsc + kFusedMaxK * CI, s_hsum + kFusedMaxK * CI,
-                    CI, gli);
+    dS.load_prepped(s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, CI, gli);
     dR.load_prepped(s_hp + kr * CI * PW, s_hsc + kr * CI, s_hsum + kr * CI, CI, gli);
     const uint4 qs[1][1] = {{dq[0]}};
     const uint32_t ss[1][1] = {{dsc[0]}};
