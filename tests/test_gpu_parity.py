@@ -564,6 +564,8 @@ ATTN_CASES = [  # (Hq, Hkv, D, Tmax, pos, rot_dim, theta) -- ragged tiles, one k
     (4, 2, 64, 40, 37, 64, 1e4),        # partial and no rotation, the full 4096-key context
     (3, 1, 128, 100, 0, 128, 1e4), (16, 1, 256, 300, 299, 64, 1e7), (8, 8, 128, 65, 64, 0, 1e4),
     (32, 2, 256, 4096, 4095, 64, 1e7),
+    (32, 2, 256, 8192, 8191, 64, 1e7),  # the benchmark's shape and launch: 128 ranges per KV head
+    (8, 1, 128, 16384, 16383, 128, 1e6),  # 256 ranges: the merge takes its loads in two batches
 ]
 
 
