@@ -13,11 +13,12 @@
 //   1. issue loads: x (staged in LDS; RMS-normalised here when the layer is given
 //      a norm weight), the shared-gate vector and its router rows (4 waves per
 //      row);
-//   2. router dots -> logits (tagged stores); then issue the shared expert's
-//      loads: one gate/up row pair per rank below I/RPWH and (into registers) the
-//      wave's shared down rows;
+//   2. router dots -> logits (tagged stores); then issue the loads of the wave's
+//      shared down rows (into registers);
 //   3. x as fixed-point planes in LDS (once per workgroup);
-//   4. shared gate/up + SwiGLU -> hs (while the other logits are in flight);
+//   4. shared gate/up + SwiGLU -> hs: its row pairs (one per rank below I/RPWH)
+//      are loaded once the logits are in (step 5), its dots run once the routed
+//      rows of step 6 are on their way;
 //   5. top-K: every thread polls its logits; from the 8 wave maxima a lower bound
 //      L of the K-th largest logit; the keys >= L go to an LDS list; one wave
 //      ranks them (larger value, then lower index) and passes the picks on;
@@ -25,26 +26,25 @@
 //   6. issue loads: two routed gate/up row pairs per wave, then (into registers)
 //      the wave's routed down rows of this workgroup's output rows;
 //   7. routed gate/up dots + SwiGLU -> hr (tagged); one tagged flag;
-//   8. wait for every workgroup's flag; read hr and hs; their planes; gamma =
-//      sigmoid(g . x); shared and routed down rows; out = residual +
+//   8. read hs; its planes; the shared down rows; the dot of gamma =
+//      sigmoid(g . x);
+//   9. read hr; its planes; the routed down rows; out = residual +
 //      sum_k w_k y_k + gamma y_shared.
 // Values that cross workgroups (logits, hs, hr) are 64-bit words (epoch << 32 |
 // value bits) written with agent-scope atomic stores (write-through to the
 // device coherence point), so they never need resetting.  The logits are polled
-// word by word.  The h values are read by every workgroup, so polling them would
-// put ~10 MB of coherent reads on a few hundred lines; instead each workgroup,
-// once all its h stores are issued, sets one tagged completion flag, and
-// consumers poll the 256 flags and then read h with ordinary cacheable loads
-// (one fetch per XCD's L2).  A word with an old epoch (a stale cached line, or a
-// store the flag overtook) is re-read coherently until it carries the current
-// one; the h buffers rotate over 4 slots so that stale lines are rare.  (One
-// shared counter instead of the flags is far slower: device-scope atomics on one
-// word serialise at ~25 ns each.)  The
-// epoch lives in the workspace: every wave of every workgroup reads it before the
-// workgroup's first barrier, every flag is tagged after that barrier, and
-// workgroup 0 advances the epoch once it has seen every flag.  Every wait is
-// bounded; on time-out a status bit is set and the output is undefined (it never
-// hangs).
+// word by word.  The h values are read by every workgroup, once its own dots are
+// done, with ordinary cacheable loads (one fetch per XCD's L2); a word with an
+// old epoch (a stale cached line, or a store not yet visible) is re-read
+// coherently until it carries the current one, and the h buffers rotate over 4
+// slots so that stale lines are rare.  (Waiting first for a tagged completion
+// flag of every workgroup, which each still writes, measured slower; one shared
+// counter instead is far slower still: device-scope atomics on one word
+// serialise at ~25 ns each.)  The epoch lives in the workspace: every wave of
+// every workgroup reads it before the workgroup's first barrier, every h word is
+// tagged after that barrier, and workgroup 0 advances the epoch once it has read
+// every h word.  Every wait is bounded; on time-out a status bit is set and the
+// output is undefined (it never hangs).
 #include <type_traits>
 
 #include "qmoe_device.h"
@@ -91,7 +91,7 @@ constexpr uint32_t kSpinLimit = 1u << 18;
 // becomes visible ~0.6 us later than one whose line has a single writer, so the
 // completion flags and each workgroup's pair of logits get a line of their own
 constexpr int kLine = 16;
-constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see step 8
+constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see steps 8 and 9
 
 // control words at the start of the workspace
 enum { CTRL_EPOCH = 0, CTRL_STATUS = 1, CTRL_ZERO = 8 };  // CTRL_ZERO is never written
@@ -177,9 +177,8 @@ __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
 // any is checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32
 // workgroups of an XCD share one fetch from memory.  A word still carrying an old
 // tag comes from a stale cached line (the buffer slot was last used several calls
-// ago) or from a store not yet visible (a flag may overtake the stores issued
-// before it): those words are re-read coherently, all of them per pass, until they
-// carry the tag (bounded; on time-out ok is cleared).
+// ago) or from a store not yet visible: those words are re-read coherently, all
+// of them per pass, until they carry the tag (bounded; on time-out ok is cleared).
 template <int PA, int PB>
 __device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uint64_t* b, int nb,
                                  float* db, uint32_t tag, bool& ok) {
@@ -637,7 +636,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // MAXR items (known since the top-K; an unused one reads a valid row it
   // ignores).  Issued here, behind the gate/up rows, so that they arrive during
   // the gate/up dots: loads return in issue order per CU, so loads issued at the
-  // end of step 7 would hold up the flag polls and h reads of step 8.  (The down
+  // end of step 7 would hold up the h reads of steps 8 and 9.  (The down
   // rows once went to LDS by DMA; after an LDS DMA the compiler makes the next use
   // of any loaded register wait for every load, DMA included.)
 #pragma unroll
@@ -686,35 +685,50 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   }
   // completion: once every wave has issued its h stores, one tagged flag, written
   // as a whole 64-byte store into a line of its own.  A bare barrier: it orders
-  // the issue only.  Waiting for the stores' acknowledgement first would cost
-  // ~0.5 us here; the flag may instead become visible before some of them, and
-  // the reader re-reads any word that still has an old tag.
+  // the issue only.  No reader waits for the flags any more (the h words carry
+  // their own tags), but the barrier and the store keep this workgroup's h reads
+  // behind its own h stores: without the barrier the layer took 15.45 us, with
+  // the barrier alone 14.60, with both 14.51.
   QMOE_PT(8);
   __builtin_amdgcn_s_barrier();
   if (tx < 8) tag_put(Lp.flags + wg * kLine + tx, 0.f, tag);
-  // ---- 8. wait for every workgroup's flag; read hr and hs; gamma; shared and
-  //         routed down rows (integer dots against the planes of h, codes in
-  //         registers since step 6);
-  //         combine
-  if ((int)tx < NB) {
-    uint32_t spins = 0;
-    while ((uint32_t)(tag_get(Lp.flags + tx * kLine) >> 32) != tag) {
-      if (++spins > kSpinLimit) {
-        ok_all = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
+  // ---- 8. the shared expert's h, read as soon as this workgroup's own routed dots
+  //         are done: every workgroup runs its shared dots before its routed ones,
+  //         so these words are nearly always current by now (each is checked by
+  //         its tag and read again until it is).  Its planes, the shared down rows
+  //         and gamma's dot then run before the wait for the routed h, not after it
+  //         (measured: 14.91 against 15.28 us per layer, 2-bit 14.16 against 14.72;
+  //         the routed planes then also fit one pass of the workgroup's threads).
+  read_done_to_lds<0, (I + kLB - 1) / kLB>(hr, 0, s_h, hs, I, s_h + K * I, tag, ok_all);
   __syncthreads();
+  prep_x_coop<BITS>(s_h + K * I, I, s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, tx, kLB);
+  __syncthreads();
+  // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
+  const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
+  if (lane == 63) s_rv[wv] = gpart;
+  if (wv < DITEMS) {  // the wave's shared down item
+    RowDot<BITS, LGI, 1> dS;
+    dS.load_prepped(s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, CI, gli);
+    const uint4 qs[1][1] = {{dq[0]}};
+    const uint32_t ss[1][1] = {{dsc[0]}};
+    float ps[1];
+    dS.template dots<1>(qs, ss, ps);
+    const float vs = group_sum_last<LGI>(ps[0]);
+    if (group_last<LGI>(lane) && nl_s < kRB) s_y[kFusedMaxK][nl_s] = vs;
+  }
   QMOE_PT(9);
-  // Every workgroup has read the epoch before tagging its flag: advance it.
+  // ---- 9. read hr, each word until it carries this call's tag; the routed down
+  //         rows (integer dots against the planes of h, codes in registers since
+  //         step 6); combine.  No wait for the flags first: polling the h words
+  //         themselves at this point measured faster (14.51 against 14.88 us per
+  //         layer, 2-bit 13.57 against 14.27).
+  QMOE_PT(10);
+  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, 0>(hr, K * I, s_h, hs, 0, s_h + K * I, tag, ok_all);
+  __syncthreads();
+  // Every workgroup read the epoch before storing its h: advance it.
   if (wg == 0 && tx == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, (I + kLB - 1) / kLB>(
-      hr, K * I, s_h, hs, I, s_h + K * I, tag, ok_all);
-  __syncthreads();
-  QMOE_PT(10);
+  QMOE_PT(11);
   if constexpr (STACK) {
     // the next layer's loads that do not depend on its input: the shared-gate
     // vector, the norm weight, the first router rows and the shared expert's rows.
@@ -732,28 +746,18 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       router_fetch(rtN, wg * 2 + (wv >> 2), rqN);
     }
   }
-  // fixed-point planes of the K + 1 h vectors, one pass over s_h (a chunk never
-  // straddles two vectors).  Only the vectors in use: with K = 4 of 8 slots, the
-  // pass over all slots cost five instead of three wave passes per SIMD.
-  prep_x_coop<BITS>(s_h, (K + 1) * I, s_hp, s_hsc, s_hsum, tx, kLB);
+  // fixed-point planes of the K routed h vectors, one pass over s_h (a chunk never
+  // straddles two vectors; only the K slots in use)
+  prep_x_coop<BITS>(s_h, K * I, s_hp, s_hsc, s_hsum, tx, kLB);
   __syncthreads();
-  QMOE_PT(11);
-  // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
-  const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
-  if (lane == 63) s_rv[wv] = gpart;
-  // down rows: the wave's shared item (waves below DITEMS) and its MAXR routed
-  // items, which all belong to one expert kw, as one branch-free block so that
-  // their plane reads, dots and reductions interleave; an item without a row holds
-  // codes that are used and then ignored
+  QMOE_PT(12);
+  // routed down rows: the wave's MAXR items, which all belong to one expert kw, as
+  // one branch-free block so that their dots and reductions interleave
   static_assert(DITEMS % MAXR == 0, "the routed down items of a wave share one expert");
   const int kw = (wv * MAXR) / DITEMS;
-  if (wv < DITEMS || kw < K) {
-    const int kr = kw < kFusedMaxK ? kw : kFusedMaxK;
-    RowDot<BITS, LGI, 1> dS, dR;
-    dS.load_prepped(s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, CI, gli);
-    dR.load_prepped(s_hp + kr * CI * PW, s_hsc + kr * CI, s_hsum + kr * CI, CI, gli);
-    const uint4 qs[1][1] = {{dq[0]}};
-    const uint32_t ss[1][1] = {{dsc[0]}};
+  if (kw < K) {
+    RowDot<BITS, LGI, 1> dR;
+    dR.load_prepped(s_hp + kw * CI * PW, s_hsc + kw * CI, s_hsum + kw * CI, CI, gli);
     uint4 qr[MAXR][1];
     uint32_t sr[MAXR][1];
 #pragma unroll
@@ -761,11 +765,8 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       qr[m][0] = dq[1 + m];
       sr[m][0] = dsc[1 + m];
     }
-    float ps[1], pr[MAXR];
-    dS.template dots<1>(qs, ss, ps);
+    float pr[MAXR];
     dR.template dots<MAXR>(qr, sr, pr);
-    // every reduction before any (lane-masked) store, so that the rows overlap
-    const float vs = group_sum_last<LGI>(ps[0]);
     float vr[MAXR];
 #pragma unroll
     for (int m = 0; m < MAXR; ++m) vr[m] = group_sum_last<LGI>(pr[m]);
@@ -775,16 +776,15 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       if (k == kw) ew = eidx[k];
     const bool eok_w = (unsigned)ew < (unsigned)E;
     if (group_last<LGI>(lane)) {
-      if (wv < DITEMS && nl_s < kRB) s_y[kFusedMaxK][nl_s] = vs;
 #pragma unroll
       for (int m = 0; m < MAXR; ++m) {
         const int nl = ((wv * MAXR + m) % DITEMS) * RPWI + subi;
-        if (kw < K && nl < kRB) s_y[kw][nl] = eok_w ? vr[m] : __builtin_nanf("");
+        if (nl < kRB) s_y[kw][nl] = eok_w ? vr[m] : __builtin_nanf("");
       }
     }
   }
   __syncthreads();
-  QMOE_PT(12);
+  QMOE_PT(13);
   if ((int)tx < kRB && row0 + (int)tx < H) {
     float gs = 0.f;
 #pragma unroll
@@ -810,9 +810,9 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     break;
   } else {
     if (++l == P.nl) break;
-    // ---- 9. (stack) the next layer's input: every workgroup's output line of this
+    // ---- 10. (stack) the next layer's input: every workgroup's output line of this
     //         layer, polled word by word until each carries this call's tag; its
-    //         other loads were issued in step 8
+    //         other loads were issued in step 9
     {
       constexpr int XW = H / kLB;  // words per thread
       uint64_t* xl = P.xbuf + (int64_t)(l - 1) * NB * kLine;
@@ -858,7 +858,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     for (int i = 0; i < CPLR; ++i) rq[i] = rqN[i];
   }
   }  // layers
-  QMOE_PT(13);
+  QMOE_PT(14);
   if (!ok_all) flag_status(A.ctrl, 1u);
   QMOE_PT_STORE();
 }
@@ -946,7 +946,7 @@ FusedCfg fused_config(const qmoe_layer& L, const void* fn) {
   FusedCfg c;
   const int E = L.routed.num_experts, K = L.top_k, H = L.routed.hidden, I = L.routed.inter;
   if (!fn || K > kFusedMaxK || E > kFusedMaxE || H % kRB) return c;
-  if (H / kRB > kLB) return c;  // every completion flag needs a polling thread
+  if (H / kRB > kLB) return c;  // at most kLB workgroups (one per CU, all co-resident)
   const int cus = device_cus();
   if (cus <= 0) return c;
   int blocks_per_cu = 0;
