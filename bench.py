@@ -66,10 +66,10 @@ def layer_bytes(bits: int) -> int:
 
 # the kernel sources each counter record depends on (a change elsewhere leaves it valid)
 TRAFFIC_SOURCES = {
-    "k_layer_w4": ["layer.hip", "qmoe_device.h"],
-    "k_layer_w2": ["layer.hip", "qmoe_device.h"],
-    "k_layer_w4_stack60": ["layer.hip", "qmoe_device.h"],
-    "expert_ffn_w4": ["kernels.hip", "qmoe_device.h"],
+    "k_layer_w4": ["layer.hip", "qmoe_handoff.h", "qmoe_device.h"],
+    "k_layer_w2": ["layer.hip", "qmoe_handoff.h", "qmoe_device.h"],
+    "k_layer_w4_stack60": ["layer.hip", "qmoe_handoff.h", "qmoe_device.h"],
+    "expert_ffn_w4": ["ffn.hip", "qmoe_handoff.h", "qmoe_device.h"],
     "batched64_w4": ["batched.hip", "kernels.hip", "qmoe_device.h"],
     "k_gdn": ["gdn.hip"],
     "k_attn_mma": ["attn.hip"],
@@ -353,7 +353,7 @@ def run_expert_ffn5(torch, q, synth, pool, seed):
                                      for _ in range(n_ring)]).astype(np.int32)).cuda()
     X = make_x_ring(torch, synth, seed, 64)
     Y = torch.empty(5, H, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(256, q.qmoe_ffn_workspace_bytes(pool, 5)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(256, q.qmoe_ffn_workspace_bytes(pool, 5)), dtype=torch.uint8, device="cuda")
     calls = [(lambda t=t: q.expert_ffn_swiglu(pool, idx[t], X[t % 64], Y, ws)) for t in range(n_ring)]
     dt = timed_steps(torch, calls, 4 * n_ring, n_ring, n_ring)
     per = 5 * expert_bytes(4) + H * 4 + 5 * H * 4
@@ -405,7 +405,7 @@ def run_ffn_bench(args, torch, q, synth):
     # a fixed pseudo-random walk over the experts (every expert visited, no repeats in a row)
     order = torch.tensor([(t * 97 + 13) % n_exp for t in range(n_ring)], dtype=torch.int32, device="cuda")
     Y = torch.empty(H, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(256, q.qmoe_ffn_workspace_bytes(pool, 1)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(256, q.qmoe_ffn_workspace_bytes(pool, 1)), dtype=torch.uint8, device="cuda")
     calls = [(lambda t=t: q.expert_ffn_swiglu(pool, order[t:t + 1], X[t], Y.view(1, H), ws))
              for t in range(n_ring)]
     steps = max(1, args.steps)
@@ -415,7 +415,7 @@ def run_ffn_bench(args, torch, q, synth):
     roof = {"bound": "hbm", "achieved": round(per_call / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(per_call / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profiles("expert_ffn_w4")}
-    extra = {"kernel": "expert_ffn_swiglu (k_ffn_gateup + k_ffn_down), roofline over the whole call",
+    extra = {"kernel": "expert_ffn_swiglu (k_ffn1: gate/up, SwiGLU and down in one launch), roofline over the call",
              "bytes_per_call": per_call, "avg_call_us": round(launch_s * 1e6, 3)}
     cpu = None
     if not args.no_cpu_baseline:

@@ -235,11 +235,13 @@ def moe_router_topk(router, x, k, logits=None, idx=None, w=None):
 
 
 def expert_ffn_swiglu(pool: ExpertPool, expert_idx, x, y=None, ws=None):
-    """y[i] = D_e(silu(G_e x) * U_e x) for e = expert_idx[i] (device int32)."""
+    """y[i] = D_e(silu(G_e x) * U_e x) for e = expert_idx[i] (device int32).  ws: a
+    workspace zero-filled before its first use and kept between calls (a fresh
+    zero-filled one when None)."""
     n = expert_idx.numel()
     y = y if y is not None else torch.empty(n, pool.hidden, dtype=torch.float32, device=x.device)
     need = qmoe_ffn_workspace_bytes(pool, n)
-    ws = ws if ws is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ws = ws if ws is not None else torch.zeros(max(need, 16), dtype=torch.uint8, device=x.device)
     _check(_lib.expert_ffn_swiglu(ctypes.byref(pool.c()), _ptr(expert_idx, torch.int32, "expert_idx"), n,
                                   _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"),
                                   _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream()),

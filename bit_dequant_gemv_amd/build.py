@@ -55,7 +55,8 @@ def _library(srcs, out, extra, verbose, jobs, build_subdir="_build"):
 
 def build_qmoe(verbose=False, jobs=None):
     csrc = os.path.join(HERE, "csrc")
-    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip", "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "ffn.hip", "layer.hip", "batched.hip",
+                                            "gdn.hip", "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
     return _library(srcs, os.path.join(HERE, "libqmoe.so"),
                     ["-I", os.path.join(ROOT, "include"), "-I", csrc], verbose,
                     jobs or min(8, os.cpu_count() or 4))
@@ -66,8 +67,8 @@ def build_probe(verbose=False, jobs=None):
     layer records per-workgroup phase timestamps (bench.py --phase-probe reads them).
     Not part of the product build."""
     csrc = os.path.join(HERE, "csrc")
-    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "layer.hip", "batched.hip", "gdn.hip",
-                                            "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "kernels.hip", "ffn.hip", "layer.hip", "batched.hip",
+                                            "gdn.hip", "attn.hip", "noalloc.hip", "stream.hip", "offload.cpp")]
     return _library(srcs, os.path.join(HERE, "libqmoe_probe.so"),
                     ["-I", os.path.join(ROOT, "include"), "-I", csrc, "-DQMOE_PHASE_PROBE"], verbose,
                     jobs or min(8, os.cpu_count() or 4), build_subdir="_build_probe")

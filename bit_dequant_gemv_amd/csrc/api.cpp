@@ -174,9 +174,12 @@ int moe_router_topk(const uint16_t* router, const float* x, int32_t T, int32_t H
                     "router launch");
 }
 
+// [0, F): the single-launch path's state (F = ffn_fused_ws_bytes, a multiple of 256);
+// [F, F + n*I*4): h of the two-launch path, so that calls with n > 1 never touch
+// the state of the n == 1 calls that share the workspace
 size_t qmoe_ffn_workspace_bytes(const qmoe_expert_pool* pool, int32_t n) {
   if (!pool || n < 0 || pool->inter < 0) return 0;
-  return (size_t)n * (size_t)pool->inter * sizeof(float);
+  return qmoe::ffn_fused_ws_bytes(*pool) + (size_t)n * (size_t)pool->inter * sizeof(float);
 }
 
 int expert_ffn_swiglu(const qmoe_expert_pool* pool, const int32_t* expert_idx, int32_t n,
@@ -192,9 +195,11 @@ int expert_ffn_swiglu(const qmoe_expert_pool* pool, const int32_t* expert_idx, i
   if (!ws || ws_bytes < qmoe_ffn_workspace_bytes(pool, n))
     return fail(QMOE_EWORKSPACE, "workspace needs %zu bytes", qmoe_ffn_workspace_bytes(pool, n));
   if (!aligned(ws, 16)) return fail(QMOE_EALIGN, "ws must be 16-byte aligned");
-  return hip_status(qmoe::launch_ffn(*pool, expert_idx, n, x, 0, y, static_cast<float*>(ws),
-                                     static_cast<hipStream_t>(stream)),
-                    "expert_ffn launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n == 1 && qmoe::ffn_fused_supported(*pool))
+    return hip_status(qmoe::launch_ffn_fused(*pool, expert_idx, x, y, ws, s), "expert_ffn launch");
+  float* h = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + qmoe::ffn_fused_ws_bytes(*pool));
+  return hip_status(qmoe::launch_ffn(*pool, expert_idx, n, x, 0, y, h, s), "expert_ffn launch");
 }
 
 int moe_combine_residual_gate(const float* y_routed, const float* topk_w, const float* y_shared,

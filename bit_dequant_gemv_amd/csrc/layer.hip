@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "qmoe_device.h"
+#include "qmoe_handoff.h"
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -86,16 +87,6 @@ constexpr int kRB = 16;          // output rows per workgroup
 constexpr int kFusedMaxK = 4;
 constexpr int kFusedMaxE = 2048;
 static_assert(kFusedMaxE % 64 == 0, "the ranking wave reads the candidate list 64 at a time");
-constexpr uint32_t kSpinLimit = 1u << 18;
-// u64 words per 128-byte line: a value written by several CUs into one shared line
-// becomes visible ~0.6 us later than one whose line has a single writer, so the
-// completion flags and each workgroup's pair of logits get a line of their own
-constexpr int kLine = 16;
-constexpr int kSlotsH = 4;  // h buffers rotate over calls (epoch % 4): see steps 8 and 9
-
-// control words at the start of the workspace
-enum { CTRL_EPOCH = 0, CTRL_STATUS = 1, CTRL_ZERO = 8 };  // CTRL_ZERO is never written
-
 struct LayerArgs {
   const uint8_t* rbase;  // routed pool
   int64_t rstride;
@@ -158,63 +149,6 @@ __device__ __forceinline__ LayerPtrs ptrs_of(const LayerArgs& A) {
           A.idx_out, A.w_out};
 }
 
-
-__device__ __forceinline__ void tag_put(uint64_t* p, float v, uint32_t tag) {
-  const uint64_t u = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
-  __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint64_t tag_get(uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
-  __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Read tagged values after their producers have all signalled that they issued
-// them: na words of a into da and nb words of b into db, every load issued before
-// any is checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32
-// workgroups of an XCD share one fetch from memory.  A word still carrying an old
-// tag comes from a stale cached line (the buffer slot was last used several calls
-// ago) or from a store not yet visible: those words are re-read coherently, all
-// of them per pass, until they carry the tag (bounded; on time-out ok is cleared).
-template <int PA, int PB>
-__device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uint64_t* b, int nb,
-                                 float* db, uint32_t tag, bool& ok) {
-  uint64_t v[PA + PB];
-  uint32_t pending = 0;
-#pragma unroll
-  for (int j = 0; j < PA + PB; ++j) {
-    const bool in_a = j < PA;
-    const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
-    v[j] = i < (in_a ? na : nb) ? (in_a ? a : b)[i] : ((uint64_t)tag << 32);
-  }
-  for (uint32_t spins = 0;; ++spins) {
-#pragma unroll
-    for (int j = 0; j < PA + PB; ++j)
-      if ((uint32_t)(v[j] >> 32) != tag) pending |= 1u << j;
-      else pending &= ~(1u << j);
-    if (!pending) break;
-    if (spins > kSpinLimit) {
-      ok = false;
-      break;
-    }
-    if (spins) __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int j = 0; j < PA + PB; ++j) {
-      const bool in_a = j < PA;
-      const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
-      if ((pending >> j) & 1u) v[j] = tag_get(const_cast<uint64_t*>(in_a ? a : b) + i);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < PA + PB; ++j) {
-    const bool in_a = j < PA;
-    const int i = threadIdx.x + (in_a ? j : j - PA) * kLB;
-    if (i < (in_a ? na : nb)) (in_a ? da : db)[i] = __uint_as_float((uint32_t)v[j]);
-  }
-}
 
 __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -699,7 +633,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         and gamma's dot then run before the wait for the routed h, not after it
   //         (measured: 14.91 against 15.28 us per layer, 2-bit 14.16 against 14.72;
   //         the routed planes then also fit one pass of the workgroup's threads).
-  read_done_to_lds<0, (I + kLB - 1) / kLB>(hr, 0, s_h, hs, I, s_h + K * I, tag, ok_all);
+  read_done_to_lds<kLB, 0, (I + kLB - 1) / kLB>(hr, 0, s_h, hs, I, s_h + K * I, tag, ok_all);
   __syncthreads();
   prep_x_coop<BITS>(s_h + K * I, I, s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, tx, kLB);
   __syncthreads();
@@ -723,7 +657,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         themselves at this point measured faster (14.51 against 14.88 us per
   //         layer, 2-bit 13.57 against 14.27).
   QMOE_PT(10);
-  read_done_to_lds<(kFusedMaxK * I + kLB - 1) / kLB, 0>(hr, K * I, s_h, hs, 0, s_h + K * I, tag, ok_all);
+  read_done_to_lds<kLB, (kFusedMaxK * I + kLB - 1) / kLB, 0>(hr, K * I, s_h, hs, 0, s_h + K * I, tag, ok_all);
   __syncthreads();
   // Every workgroup read the epoch before storing its h: advance it.
   if (wg == 0 && tx == 0)

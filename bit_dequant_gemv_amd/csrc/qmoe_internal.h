@@ -22,6 +22,13 @@ hipError_t launch_qgemv(int bits, const uint8_t* codes, const uint32_t* sb, cons
 
 hipError_t launch_ffn(const qmoe_expert_pool& pool, const int32_t* idx, int n, const float* x,
                       int64_t x_stride, float* y, float* h_ws, hipStream_t s);
+// One expert's FFN in a single launch (ffn.hip), for the shapes ffn_fused_supported
+// accepts.  ws: ffn_fused_ws_bytes(pool) bytes, zero-filled before its first use and
+// kept between calls (a call counter and tagged h values).
+bool ffn_fused_supported(const qmoe_expert_pool& pool);
+size_t ffn_fused_ws_bytes(const qmoe_expert_pool& pool);
+hipError_t launch_ffn_fused(const qmoe_expert_pool& pool, const int32_t* idx, const float* x, float* y,
+                            void* ws, hipStream_t s);
 
 // prep_bits = 4 or 2 with xplanes: the router may also write the fixed-point x
 // planes of every token (pw words per token); *prepped says whether it did.

@@ -127,8 +127,18 @@ int moe_router_topk(const uint16_t* router, const float* x, int32_t T, int32_t H
  * Expert FFN with fused SwiGLU for n experts of a pool, chosen by a device index list
  * ([PK] Metal shaders: dequant matvec + fused SwiGLU):
  *   y[i] = D_e (silu(G_e x) * (U_e x)),  e = expert_idx[i]
- *   expert_idx: device int32 [n]; x: device float [H]; y: device float [n][H] (written)
- *   ws: device scratch of at least qmoe_ffn_workspace_bytes(pool, n) bytes.
+ *   expert_idx: device int32 [n]; x: device float [H]; y: device float [n][H] (written);
+ *   an index outside [0, num_experts) gives a row of NaN.
+ *   ws: device workspace of at least qmoe_ffn_workspace_bytes(pool, n) bytes, 16-byte
+ *   aligned, ZERO-FILLED before its first use.  With n == 1 and a shape the
+ *   single-launch kernel takes (hidden 1024/2048/4096, inter 256/512/1024) the call
+ *   is one launch that keeps state in the workspace from call to call (a call
+ *   counter, values tagged with the call number, as moe_layer_forward does), so the
+ *   caller must not write to its first qmoe_ffn_workspace_bytes(pool, 0) bytes
+ *   afterwards; calls that share a workspace must be stream-ordered.  Word 1 (int32
+ *   at byte offset 4) is then a status word: nonzero if a bounded wait inside the
+ *   kernel ran out (the output of that call is undefined).  Otherwise two launches
+ *   use the rest of the workspace as scratch.
  */
 int expert_ffn_swiglu(const qmoe_expert_pool* pool, const int32_t* expert_idx, int32_t n,
                       const float* x, float* y, void* ws, size_t ws_bytes, void* stream);

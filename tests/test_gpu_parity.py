@@ -134,6 +134,56 @@ def test_expert_ffn_parity(q, H, I, bits, E, idx):
         assert r <= TOL and r <= TIGHT
 
 
+# one expert per call on a shape the single-launch kernel takes (hidden 1024/2048/4096,
+# inter 256/512/1024): gate/up, SwiGLU and down in one launch, h handed over as tagged
+# words; both bit widths, the smallest and largest grids and both lane layouts
+FUSED_FFN_CASES = [(1024, 256, 4, 3, 2), (2048, 512, 2, 2, 1), (4096, 1024, 2, 2, 0), (1024, 1024, 4, 2, 1),
+                   (4096, 256, 4, 2, 1), (1024, 256, 2, 2, 1), (4096, 1024, 4, 3, 2)]
+
+
+@pytest.mark.parametrize("H,I,bits,E,e", FUSED_FFN_CASES)
+def test_expert_ffn_single_launch_parity(q, H, I, bits, E, e):
+    """n = 1 takes the single-launch kernel: against the oracle, over nine calls on one
+    workspace (the call counter passes the four h slots twice), with a call of three
+    experts (the two-launch path, sharing the workspace) in the middle; the status
+    word stays clear."""
+    say("expert_ffn single launch", H, I, bits, E, e)
+    seed = 1100 + H + I + bits
+    pool = q.ExpertPool.allocate(E, H, I, bits)
+    synth.fill_expert_pool(pool.buf, pool.stride, E, 0, 0, seed, H, I, bits)
+    ws = torch.zeros(q.qmoe_ffn_workspace_bytes(pool, 3), dtype=torch.uint8, device="cuda")
+    blocks = [synth.expert_block(seed, 0, k, H, I, bits) for k in range(E)]
+    for call in range(9):
+        x = host_x(seed, call, H)
+        ek = (e + call) % E
+        if call == 4:
+            idx = [ek, (ek + 1) % E, ek]
+            y = q.expert_ffn_swiglu(pool, torch.tensor(idx, dtype=torch.int32, device="cuda"),
+                                    torch.from_numpy(x).cuda(), ws=ws).cpu().numpy()
+        else:
+            idx = [ek]
+            y = q.expert_ffn_swiglu(pool, torch.tensor(idx, dtype=torch.int32, device="cuda"),
+                                    torch.from_numpy(x).cuda(), ws=ws).cpu().numpy()
+        for i, k in enumerate(idx):
+            r = _rel(y[i], oracle.expert_ffn(blocks[k], x, H, I, bits))
+            say("  call", call, "slot", i, "expert", k, "rel_l2", r)
+            assert r <= TOL and r <= TIGHT
+    assert int(ws[4:8].view(torch.int32).item()) == 0  # status word
+
+
+def test_expert_ffn_single_launch_bad_index_gives_nan(q):
+    say("expert_ffn single launch, bad index")
+    pool = q.ExpertPool.allocate(2, 4096, 1024, 4)
+    synth.fill_expert_pool(pool.buf, pool.stride, 2, 0, 0, 3, 4096, 1024, 4)
+    ws = torch.zeros(q.qmoe_ffn_workspace_bytes(pool, 1), dtype=torch.uint8, device="cuda")
+    x = torch.from_numpy(host_x(3, 0, 4096)).cuda()
+    for idx, finite in (([7], False), ([1], True), ([-1], False), ([0], True)):
+        y = q.expert_ffn_swiglu(pool, torch.tensor(idx, dtype=torch.int32, device="cuda"), x, ws=ws)
+        y = y.cpu().numpy()
+        assert np.isfinite(y).all() if finite else np.isnan(y).all()
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+
+
 def test_expert_ffn_bad_index_gives_nan(q):
     say("expert_ffn bad index")
     pool = q.ExpertPool.allocate(2, 256, 128, 4)
