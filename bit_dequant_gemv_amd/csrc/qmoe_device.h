@@ -201,8 +201,13 @@ __device__ __forceinline__ void chunk_exp(float m, float& f, float& scale) {
   }
 }
 
+// rint(x*f) + 2^23 in two instructions: |x*f| < 2^22 and x*f is exact (f is a power
+// of two), so fma(x, f, 1.5*2^23) lands in [2^23, 2^24), where the spacing of
+// floats is 1: the single rounding of the fma is round-to-nearest-even of x*f, and
+// the float's bits are 0x4B000000 + 2^22 + rint(x*f).  (A chunk with Inf/NaN has
+// f = 0 and a NaN scale: its words are don't-cares.)
 __device__ __forceinline__ uint32_t to_u24(float x, float f) {
-  return (uint32_t)((int)rintf(x * f) + (1 << 23));
+  return __float_as_uint(fmaf(x, f, 12582912.0f)) - 0x4AC00000u;
 }
 
 // Nibble transpose of eight 24-bit values: out[d] holds digit d (bits 4d..4d+3) of
