@@ -184,6 +184,26 @@ def test_expert_ffn_single_launch_bad_index_gives_nan(q):
     assert int(ws[4:8].view(torch.int32).item()) == 0
 
 
+def test_expert_ffn_single_launch_counter_wraps(q):
+    """The one-launch FFN's call counter wraps past 2^32 - 1 without taking a
+    zero-filled h word for a current one."""
+    say("expert_ffn single launch, counter wrap")
+    H, I, bits, E, seed = 2048, 512, 4, 2, 1234
+    pool = q.ExpertPool.allocate(E, H, I, bits)
+    synth.fill_expert_pool(pool.buf, pool.stride, E, 0, 0, seed, H, I, bits)
+    ws = torch.zeros(q.qmoe_ffn_workspace_bytes(pool, 1), dtype=torch.uint8, device="cuda")
+    ws[0:4].view(torch.int32).fill_(-2)  # counter = 0xFFFFFFFE
+    for call in range(3):
+        x = host_x(seed, call, H)
+        y = q.expert_ffn_swiglu(pool, torch.tensor([call % E], dtype=torch.int32, device="cuda"),
+                                torch.from_numpy(x).cuda(), ws=ws).cpu().numpy()
+        ref = oracle.expert_ffn(synth.expert_block(seed, 0, call % E, H, I, bits), x, H, I, bits)
+        assert _rel(y[0], ref) <= TIGHT
+    # 0xFFFFFFFE -> 0xFFFFFFFF -> 1 (0 skipped) -> 2
+    assert int(ws[0:4].view(torch.int32).item()) == 2
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+
+
 def test_expert_ffn_bad_index_gives_nan(q):
     say("expert_ffn bad index")
     pool = q.ExpertPool.allocate(2, 256, 128, 4)
