@@ -619,10 +619,10 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   }
   // completion: once every wave has issued its h stores, one tagged flag, written
   // as a whole 64-byte store into a line of its own.  A bare barrier: it orders
-  // the issue only.  No reader waits for the flags any more (the h words carry
-  // their own tags), but the barrier and the store keep this workgroup's h reads
-  // behind its own h stores: without the barrier the layer took 15.45 us, with
-  // the barrier alone 14.60, with both 14.51.
+  // the issue only.  No reader waits for the flags (the h words carry their own
+  // tags), but the barrier and the store keep this workgroup's h reads behind its
+  // own h stores: without the barrier the layer took 15.45 us, with the barrier
+  // alone 14.60, with both 14.51.
   QMOE_PT(8);
   __builtin_amdgcn_s_barrier();
   if (tx < 8) tag_put(Lp.flags + wg * kLine + tx, 0.f, tag);
