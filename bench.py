@@ -671,7 +671,7 @@ def run_batched_bench(args, torch, q, synth):
 PHASES = ["start", "x in LDS", "router dots done", "x planes in LDS", "x planes in registers",
           "logits polled", "top-K ranked", "shared and routed rows issued",
           "shared + routed gate/up done (wave 0)", "shared h, planes and down rows", "routed h read starts",
-          "routed h in LDS", "routed h planes", "routed down rows", "end"]
+          "routed h read into planes", "epoch advanced (barrier)", "routed down rows", "end"]
 
 
 def run_phase_probe(args, torch, q, synth):

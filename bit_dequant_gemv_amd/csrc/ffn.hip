@@ -14,8 +14,8 @@
 //      workgroup's output rows;
 //   2. x as fixed-point planes in LDS, then in registers;
 //   3. gate/up dots + SwiGLU -> h (tagged stores);
-//   4. h read back by every workgroup, each word until it carries this call's
-//      number; its planes; the down rows -> y.
+//   4. h read by every workgroup straight into its planes (no LDS copy of the
+//      values), each word until it carries this call's number; the down rows -> y.
 // The down rows travel during steps 2-3 instead of being requested after a kernel
 // boundary, and the boundary itself (launch gap, the second kernel's first load of
 // h) becomes one read of tagged words.
@@ -78,7 +78,6 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
   __shared__ __align__(16) float s_x[H];
   __shared__ uint32_t s_xp[CH * PW];
   __shared__ float s_xsc[CH], s_xsum[CH];
-  __shared__ __align__(16) float s_h[I];
   __shared__ __align__(16) uint32_t s_hp[CI * PW];
   __shared__ float s_hsc[CI], s_hsum[CI];
   bool ok = true;
@@ -94,8 +93,17 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
   const int xi = min(tx, H / 8 - 1);
   const float4 x0 = reinterpret_cast<const float4*>(A.x + 8 * xi)[0];
   const float4 x1 = reinterpret_cast<const float4*>(A.x + 8 * xi)[1];
-  const bool has = rank < NSP;
-  const int j = has ? rank * RPWH + subh : subh;  // no item: rows of item 0, ignored
+  // h layout: workgroup b = e * Q + q owns the line b * kLine, whose word i holds
+  // h value EPW * (SPW * q + i) + e (i < SPW): value e of code words SPW*q .. +SPW.
+  // So each line has a single writer, and the thread that builds code word t's
+  // planes reads its EPW values at one stride, the lanes of a wave in runs of SPW
+  // contiguous words.
+  constexpr int EPW = QTraits<BITS>::EPW;
+  constexpr int SPW = I / NB;              // h words per workgroup
+  constexpr int Q = I / EPW / SPW;         // workgroups per value position e
+  static_assert(SPW * NB == I && Q * EPW == NB && SPW % RPWH == 0, "h layout");
+  const bool has = rank < NSP;  // item wv of this workgroup: words wv*RPWH .. +RPWH
+  const int j = has ? EPW * (SPW * (wg % Q) + wv * RPWH + subh) + wg / Q : subh;  // no item: ignored
   RowDot<BITS, LGH, CPLH> dH;
   uint4 q[2][CPLH];
   uint32_t sq[2][CPLH];
@@ -124,24 +132,12 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
   // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
   uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)epoch) + 1u;
   tag = tag ? tag : 1u;
-  // h value j (item j / RPWH, row j % RPWH) lives in the line of the workgroup
-  // that computes it, since a line with a single writer becomes visible to other
-  // CUs sooner than one written by several; every workgroup reads the lines back in
-  // buffer order, so that a wave's loads stay coalesced (measured per call: 8.10 us,
-  // against 8.46 with h in row order, 16 writers per line, and 8.27 for the two
-  // launches of kernels.hip)
+  // h lives in lines with a single writer, since such a line becomes visible to
+  // other CUs sooner than one written by several (measured per call, 4096 x 1024
+  // 4-bit: 7.40 us with the layout above read straight into planes; 8.03 with
+  // single-writer lines read in buffer order into LDS; 8.46 with h in row order,
+  // 16 writers per line; 8.27 for the two launches of kernels.hip)
   uint64_t* hb = A.h + (int64_t)(tag % kSlotsH) * H;
-  auto hpos = [](int jv) {
-    const int r = jv / RPWH;
-    return (r % NB) * kLine + (r / NB) * RPWH + jv % RPWH;
-  };
-  // read back in buffer order: slot t is word t % SPW of workgroup t / SPW's line
-  constexpr int SPW = I / NB;  // h words per workgroup
-  auto rd_pos = [](int t) { return (t / SPW) * kLine + t % SPW; };
-  auto rd_val = [](int t) {
-    const int off = t % SPW;
-    return ((off / RPWH) * NB + t / SPW) * RPWH + off % RPWH;
-  };
 
   // ---- 3. gate/up dots + SwiGLU -> h
   if (has) {
@@ -149,20 +145,25 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
     dH.template dots<2>(q, sq, p);
     const float a = group_sum_last<LGH>(p[0]);
     const float u = group_sum_last<LGH>(p[1]);
-    if (group_last<LGH>(lane)) tag_put(hb + hpos(j), eok ? silu_f(a) * u : __builtin_nanf(""), tag);
+    if (group_last<LGH>(lane)) tag_put(hb + wg * kLine + wv * RPWH + subh, eok ? silu_f(a) * u : __builtin_nanf(""), tag);
   }
 
-  // ---- 4. h back (the barrier keeps the reads behind this workgroup's own h
-  //         stores), its planes, the down rows
+  // ---- 4. h read straight into its planes (the barrier keeps the reads behind
+  //         this workgroup's own h stores): thread t takes code word t; the down
+  //         rows
   __builtin_amdgcn_s_barrier();
-  read_tagged_map<kFB, (I + kFB - 1) / kFB>(hb, I, rd_pos, rd_val, s_h, tag, ok);
+  static_assert(I / EPW <= kFB, "one code word of h per thread");
+  if (wv * 64 < I / EPW) {
+    const bool valid = tx < I / EPW;
+    float v[EPW];
+    read_tagged_strided<EPW>(hb + (tx / SPW) * kLine + tx % SPW, Q * kLine, valid, v, tag, ok);
+    prep_x_word<BITS>(v, valid, tx, s_hp, s_hsc, s_hsum);
+  }
   __syncthreads();
   // Every workgroup read the counter before storing its h (each stores at least
   // one word: rank wg < I/RPWH): advance it.
   if (wg == 0 && tx == 0)
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prep_x_coop<BITS>(s_h, I, s_hp, s_hsc, s_hsum, tx, kFB);
-  __syncthreads();
   if (wv < DITEMS) {
     RowDot<BITS, LGI, 1> dD;
     dD.load_prepped(s_hp, s_hsc, s_hsum, CI, gli);

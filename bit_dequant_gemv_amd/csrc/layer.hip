@@ -26,9 +26,9 @@
 //   6. issue loads: two routed gate/up row pairs per wave, then (into registers)
 //      the wave's routed down rows of this workgroup's output rows;
 //   7. routed gate/up dots + SwiGLU -> hr (tagged); one tagged flag;
-//   8. read hs; its planes; the shared down rows; the dot of gamma =
-//      sigmoid(g . x);
-//   9. read hr; its planes; the routed down rows; out = residual +
+//   8. hs read straight into its planes (no LDS copy of the values); the shared
+//      down rows; the dot of gamma = sigmoid(g . x);
+//   9. hr read into its planes the same way; the routed down rows; out = residual +
 //      sum_k w_k y_k + gamma y_shared.
 // Values that cross workgroups (logits, hs, hr) are 64-bit words (epoch << 32 |
 // value bits) written with agent-scope atomic stores (write-through to the
@@ -104,8 +104,8 @@ struct LayerArgs {
   uint32_t* ctrl;
   uint64_t* logits;  // [E/2][kLine]: logit e is word e % 2 of line e / 2
   uint64_t* flags;   // [NB][kLine]: workgroup b has issued all its h stores
-  uint64_t* hs;      // [kSlotsH][I]
-  uint64_t* hr;      // [kSlotsH][K][I]
+  uint64_t* hs;      // [kSlotsH][I], word-transposed (see hpos in k_layer)
+  uint64_t* hr;      // [kSlotsH][kFusedMaxK * I], word-transposed
   int E, K;
 };
 
@@ -204,7 +204,6 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   __shared__ __align__(16) float s_x[H];          // the layer input x
   __shared__ uint32_t s_xp[CH * PW];
   __shared__ float s_xsc[CH], s_xsum[CH];
-  __shared__ __align__(16) float s_h[(kFusedMaxK + 1) * I];  // routed h (k < K), shared h (k = K)
   __shared__ __align__(16) uint32_t s_hp[(kFusedMaxK + 1) * CI * PW];  // their planes
   __shared__ float s_hsc[(kFusedMaxK + 1) * CI], s_hsum[(kFusedMaxK + 1) * CI];
   __shared__ float s_y[kFusedMaxK + 1][kRB];
@@ -397,6 +396,11 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
 
   uint64_t* hs = Lp.hs + (size_t)(tag % kSlotsH) * I;
   uint64_t* hr = Lp.hr + (size_t)(tag % kSlotsH) * kFusedMaxK * I;
+  // h is kept word-transposed: value e of code-word-sized group w of a vector
+  // lives at e * (words in the vector) + w, so that the thread that builds word
+  // w's planes reads its values with loads that are contiguous across the wave.
+  constexpr int kHsW = I / QTraits<BITS>::EPW, kHrW = kFusedMaxK * I / QTraits<BITS>::EPW;
+  auto hpos = [](int j, int words) { return (j % QTraits<BITS>::EPW) * words + j / QTraits<BITS>::EPW; };
   // the first poll of logits 0..kLB-1 (step 5) goes out now, unconditionally (a
   // lane past E reads logit E - 1), so that its round trip overlaps the loading of
   // the x planes; logits from kLB on are first read by the poll loop of step 5
@@ -596,7 +600,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     const float a = group_sum_last<LGH>(p[0]);
     const float u = group_sum_last<LGH>(p[1]);
     hs_val = silu_f(a) * u;
-    if (group_last<LGH>(lane)) tag_put(hs + jsp, hs_val, tag);
+    if (group_last<LGH>(lane)) tag_put(hs + hpos(jsp, kHsW), hs_val, tag);
   }
   // ---- 7. routed gate/up dots + SwiGLU -> hr, two row pairs per step (the first
   //         step outside the loop, so that its dots wait for their own rows only,
@@ -609,7 +613,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       const float a = group_sum_last<LGH>(p[2 * v]);
       const float u = group_sum_last<LGH>(p[2 * v + 1]);
       if (group_last<LGH>(lane) && it0 + v * W < n_rp)
-        tag_put(hr + kk[v] * I + jj[v], eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
+        tag_put(hr + hpos(kk[v] * I + jj[v], kHrW), eok[v] ? silu_f(a) * u : __builtin_nanf(""), tag);
     }
   };
   if (it < n_rp) gate_up_step(it);
@@ -617,6 +621,22 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     fetch_pairs(it);
     gate_up_step(it);
   }
+  // the planes of n h values (n a multiple of a chunk) built straight from
+  // registers: thread t reads the values of code word t, tagged words
+  // src[e * stride + t] (e < EPW); one DPP quad holds a chunk; a wave with no word
+  // in a pass skips it.
+  auto h_planes = [&](const uint64_t* src, int stride, int n, uint32_t* planes, float* scl, float* xsum) {
+    constexpr int EPW = QTraits<BITS>::EPW;
+    const int words = n / EPW;
+    for (int w0 = 0; w0 < words; w0 += kLB) {
+      if (w0 + (int)wv * 64 >= words) break;
+      const int w = w0 + (int)tx;
+      const bool valid = w < words;
+      float v[EPW];
+      read_tagged_strided<EPW>(src + w, stride, valid, v, tag, ok_all);
+      prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
+    }
+  };
   // completion: once every wave has issued its h stores, one tagged flag, written
   // as a whole 64-byte store into a line of its own.  A bare barrier: it orders
   // the issue only.  No reader waits for the flags (the h words carry their own
@@ -633,9 +653,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         and gamma's dot then run before the wait for the routed h, not after it
   //         (measured: 14.91 against 15.28 us per layer, 2-bit 14.16 against 14.72;
   //         the routed planes then also fit one pass of the workgroup's threads).
-  read_done_to_lds<kLB, 0, (I + kLB - 1) / kLB>(hr, 0, s_h, hs, I, s_h + K * I, tag, ok_all);
-  __syncthreads();
-  prep_x_coop<BITS>(s_h + K * I, I, s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, tx, kLB);
+  h_planes(hs, kHsW, I, s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI);
   __syncthreads();
   // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
   const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
@@ -657,11 +675,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         themselves at this point measured faster (14.51 against 14.88 us per
   //         layer, 2-bit 13.57 against 14.27).
   QMOE_PT(10);
-  read_done_to_lds<kLB, (kFusedMaxK * I + kLB - 1) / kLB, 0>(hr, K * I, s_h, hs, 0, s_h + K * I, tag, ok_all);
-  __syncthreads();
-  // Every workgroup read the epoch before storing its h: advance it.
-  if (wg == 0 && tx == 0)
-    __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  h_planes(hr, kHrW, K * I, s_hp, s_hsc, s_hsum);
   QMOE_PT(11);
   if constexpr (STACK) {
     // the next layer's loads that do not depend on its input: the shared-gate
@@ -680,10 +694,10 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       router_fetch(rtN, wg * 2 + (wv >> 2), rqN);
     }
   }
-  // fixed-point planes of the K routed h vectors, one pass over s_h (a chunk never
-  // straddles two vectors; only the K slots in use)
-  prep_x_coop<BITS>(s_h, K * I, s_hp, s_hsc, s_hsum, tx, kLB);
   __syncthreads();
+  // Every workgroup read the epoch before storing its h: advance it.
+  if (wg == 0 && tx == 0)
+    __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   QMOE_PT(12);
   // routed down rows: the wave's MAXR items, which all belong to one expert kw, as
   // one branch-free block so that their dots and reductions interleave

@@ -310,6 +310,40 @@ __device__ __forceinline__ float chunk_dot<2>(const uint4 c, const uint32_t* P) 
   return combine_planes(a, qs);
 }
 
+// The planes of word w (EPW values v, zeros when !valid) of an input vector, the
+// chunk scale and the chunk sum: lanes w..w+3 of one DPP quad hold the 4 words of
+// a chunk, and all four must call this together.
+template <int BITS>
+__device__ __forceinline__ void prep_x_word(const float (&v)[QTraits<BITS>::EPW], bool valid, int w,
+                                            uint32_t* planes, float* scl, float* xsum) {
+  constexpr int EPW = QTraits<BITS>::EPW;
+  constexpr int NPW = BITS == 4 ? 6 : 12;  // plane words per code word
+  float m = 0.f, s = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPW; j += 4) {
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j]), fabsf(v[j + 1])), fmaxf(fabsf(v[j + 2]), fabsf(v[j + 3]))));
+    s += (v[j] + v[j + 1]) + (v[j + 2] + v[j + 3]);
+  }
+  // a chunk is 4 consecutive words = 4 consecutive lanes (one DPP quad)
+  m = fmaxf(m, dpp_f<kDppXor1>(m));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  s += dpp_f<kDppXor1>(s);
+  s += dpp_f<kDppXor2>(s);
+  float f, scale;
+  chunk_exp(m, f, scale);
+  if (valid) {
+    uint32_t p[NPW];
+    prep_word<BITS>(v, f, p);
+    const int c = w >> 2, i = w & 3;
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) planes[c * QTraits<BITS>::PW + i * NPW + k] = p[k];
+    if (i == 0) {
+      scl[c] = scale * QTraits<BITS>::FACTOR;
+      xsum[c] = s;
+    }
+  }
+}
+
 // Workgroup-cooperative preparation of the x planes of a whole input vector into
 // shared memory: planes[c*PW ...], scl[c] (chunk scale, 2-bit 1/4 included) and
 // xsum[c] (plain sum of the chunk's x) for chunks c < n/EPC.  Every thread of the
@@ -318,13 +352,11 @@ template <int BITS>
 __device__ __forceinline__ void prep_x_coop(const float* x, int n, uint32_t* planes, float* scl,
                                             float* xsum, int tid, int nthreads) {
   constexpr int EPW = QTraits<BITS>::EPW;
-  constexpr int NPW = BITS == 4 ? 6 : 12;  // plane words per code word
   const int words = n / EPW;
   for (int w0 = 0; w0 < words; w0 += nthreads) {
     const int w = w0 + tid;
     const bool valid = w < words;
     float v[EPW];
-    float m = 0.f, s = 0.f;
 #pragma unroll
     for (int j = 0; j < EPW; j += 4) {
       float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -333,27 +365,8 @@ __device__ __forceinline__ void prep_x_coop(const float* x, int n, uint32_t* pla
       v[j + 1] = f4.y;
       v[j + 2] = f4.z;
       v[j + 3] = f4.w;
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(f4.x), fabsf(f4.y)), fmaxf(fabsf(f4.z), fabsf(f4.w))));
-      s += (f4.x + f4.y) + (f4.z + f4.w);
     }
-    // a chunk is 4 consecutive words = 4 consecutive lanes (one DPP quad)
-    m = fmaxf(m, dpp_f<kDppXor1>(m));
-    m = fmaxf(m, dpp_f<kDppXor2>(m));
-    s += dpp_f<kDppXor1>(s);
-    s += dpp_f<kDppXor2>(s);
-    float f, scale;
-    chunk_exp(m, f, scale);
-    if (valid) {
-      uint32_t p[NPW];
-      prep_word<BITS>(v, f, p);
-      const int c = w >> 2, i = w & 3;
-#pragma unroll
-      for (int k = 0; k < NPW; ++k) planes[c * QTraits<BITS>::PW + i * NPW + k] = p[k];
-      if (i == 0) {
-        scl[c] = scale * QTraits<BITS>::FACTOR;
-        xsum[c] = s;
-      }
-    }
+    prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
   }
 }
 

@@ -39,28 +39,25 @@ __device__ __forceinline__ void flag_status(uint32_t* ctrl, uint32_t bit) {
   __hip_atomic_fetch_or(ctrl + CTRL_STATUS, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Read tagged values (NT threads per workgroup, each taking words threadIdx.x +
-// j*NT): na words of a into da and nb words of b into db, every load issued before
-// any is checked (one round trip).  Ordinary (L2-cacheable) loads, so the 32
-// workgroups of an XCD share one fetch from memory.  A word still carrying an old
-// tag comes from a stale cached line (the buffer slot was last used several calls
-// ago) or from a store not yet visible: those words are re-read coherently, all
-// of them per pass, until they carry the tag (bounded; on time-out ok is cleared).
-template <int NT, int PA, int PB>
-__device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uint64_t* b, int nb,
-                                 float* db, uint32_t tag, bool& ok) {
-  uint64_t v[PA + PB];
-  uint32_t pending = 0;
+// Read N tagged words src[j * stride] (j < N) into v (their values), every load
+// issued before any is checked (one round trip); nothing is read when !valid (v is
+// then zeros).  Ordinary (L2-cacheable) loads, so the 32 workgroups of an XCD
+// share one fetch from memory.  A word still carrying an old tag comes from a
+// stale cached line (the buffer slot was last used several calls ago) or from a
+// store not yet visible: those words are re-read coherently, all of them per
+// pass, until they carry the tag (bounded; on time-out ok is cleared).
+template <int N>
+__device__ __forceinline__ void read_tagged_strided(const uint64_t* src, int stride, bool valid, float (&v)[N],
+                                                    uint32_t tag, bool& ok) {
+  static_assert(N <= 32, "at most 32 words");
+  uint64_t r[N];
 #pragma unroll
-  for (int j = 0; j < PA + PB; ++j) {
-    const bool in_a = j < PA;
-    const int i = threadIdx.x + (in_a ? j : j - PA) * NT;
-    v[j] = i < (in_a ? na : nb) ? (in_a ? a : b)[i] : ((uint64_t)tag << 32);
-  }
+  for (int j = 0; j < N; ++j) r[j] = valid ? src[(int64_t)j * stride] : ((uint64_t)tag << 32);
+  uint32_t pending = 0;
   for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
-    for (int j = 0; j < PA + PB; ++j)
-      if ((uint32_t)(v[j] >> 32) != tag) pending |= 1u << j;
+    for (int j = 0; j < N; ++j)
+      if ((uint32_t)(r[j] >> 32) != tag) pending |= 1u << j;
       else pending &= ~(1u << j);
     if (!pending) break;
     if (spins > kSpinLimit) {
@@ -69,53 +66,11 @@ __device__ void read_done_to_lds(const uint64_t* a, int na, float* da, const uin
     }
     if (spins) __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-    for (int j = 0; j < PA + PB; ++j) {
-      const bool in_a = j < PA;
-      const int i = threadIdx.x + (in_a ? j : j - PA) * NT;
-      if ((pending >> j) & 1u) v[j] = tag_get(const_cast<uint64_t*>(in_a ? a : b) + i);
-    }
+    for (int j = 0; j < N; ++j)
+      if ((pending >> j) & 1u) r[j] = tag_get(const_cast<uint64_t*>(src) + (int64_t)j * stride);
   }
 #pragma unroll
-  for (int j = 0; j < PA + PB; ++j) {
-    const bool in_a = j < PA;
-    const int i = threadIdx.x + (in_a ? j : j - PA) * NT;
-    if (i < (in_a ? na : nb)) (in_a ? da : db)[i] = __uint_as_float((uint32_t)v[j]);
-  }
-}
-
-// The same in the order of the buffer: slot t = threadIdx.x + j*NT (t < n, j < P)
-// reads word src[pos(t)] and stores it at dst[val(t)], so that consecutive threads
-// read consecutive words; a slot with val(t) < 0 is padding (not waited for).
-template <int NT, int P, class Pos, class Val>
-__device__ void read_tagged_map(const uint64_t* src, int n, Pos pos, Val val, float* dst, uint32_t tag,
-                                bool& ok) {
-  uint64_t v[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int t = threadIdx.x + j * NT;
-    v[j] = (t < n && val(t) >= 0) ? src[pos(t)] : ((uint64_t)tag << 32);
-  }
-  uint32_t pending = 0;
-  for (uint32_t spins = 0;; ++spins) {
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-      if ((uint32_t)(v[j] >> 32) != tag) pending |= 1u << j;
-      else pending &= ~(1u << j);
-    if (!pending) break;
-    if (spins > kSpinLimit) {
-      ok = false;
-      break;
-    }
-    if (spins) __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-      if ((pending >> j) & 1u) v[j] = tag_get(const_cast<uint64_t*>(src) + pos(threadIdx.x + j * NT));
-  }
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int t = threadIdx.x + j * NT;
-    if (t < n && val(t) >= 0) dst[val(t)] = __uint_as_float((uint32_t)v[j]);
-  }
+  for (int j = 0; j < N; ++j) v[j] = __uint_as_float((uint32_t)r[j]);
 }
 
 }  // namespace
