@@ -384,7 +384,25 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   shared_down_fetch(Lp.sblk, dq[0], dsc[0]);
 
   // ---- 3. x planes in LDS; the epoch goes to every thread through the barrier
-  prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
+  if constexpr (BITS == 2) {
+    // half a code word per thread (8 values, elements 2k + h of word t >> 1)
+    for (int t0 = 0; t0 < H / 8; t0 += kLB) {
+      if (t0 + (int)wv * 64 >= H / 8) break;
+      const int t = t0 + (int)tx;
+      const bool valid = t < H / 8;
+      const float4* xp = reinterpret_cast<const float4*>(s_x + 16 * (valid ? t >> 1 : 0));
+      const float4 a = xp[0], b = xp[1], c = xp[2], d = xp[3];
+      const bool odd = (t & 1) != 0;
+      const float v[8] = {odd ? a.y : a.x, odd ? a.w : a.z, odd ? b.y : b.x, odd ? b.w : b.z,
+                          odd ? c.y : c.x, odd ? c.w : c.z, odd ? d.y : d.x, odd ? d.w : d.z};
+      float vz[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vz[k] = valid ? v[k] : 0.f;
+      prep_x_half2(vz, valid, t, s_xp, s_xsc, s_xsum);
+    }
+  } else {
+    prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
+  }
   if (tx == 0) {
     s_tag = tag0;
     s_ncand = 0;
@@ -625,16 +643,31 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   // registers: thread t reads the values of code word t, tagged words
   // src[e * stride + t] (e < EPW); one DPP quad holds a chunk; a wave with no word
   // in a pass skips it.
+  // 2-bit: half a code word per thread instead (8 values: elements 2k + h of word
+  // t >> 1, at stride 2 * stride from src[h * stride + (t >> 1)]), so that twice the
+  // threads each read and convert half as many values.
   auto h_planes = [&](const uint64_t* src, int stride, int n, uint32_t* planes, float* scl, float* xsum) {
-    constexpr int EPW = QTraits<BITS>::EPW;
-    const int words = n / EPW;
-    for (int w0 = 0; w0 < words; w0 += kLB) {
-      if (w0 + (int)wv * 64 >= words) break;
-      const int w = w0 + (int)tx;
-      const bool valid = w < words;
-      float v[EPW];
-      read_tagged_strided<EPW>(src + w, stride, valid, v, tag, ok_all);
-      prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
+    if constexpr (BITS == 2) {
+      const int halves = n / 8;
+      for (int t0 = 0; t0 < halves; t0 += kLB) {
+        if (t0 + (int)wv * 64 >= halves) break;
+        const int t = t0 + (int)tx;
+        const bool valid = t < halves;
+        float v[8];
+        read_tagged_strided<8>(src + (t & 1) * stride + (t >> 1), 2 * stride, valid, v, tag, ok_all);
+        prep_x_half2(v, valid, t, planes, scl, xsum);
+      }
+    } else {
+      constexpr int EPW = QTraits<BITS>::EPW;
+      const int words = n / EPW;
+      for (int w0 = 0; w0 < words; w0 += kLB) {
+        if (w0 + (int)wv * 64 >= words) break;
+        const int w = w0 + (int)tx;
+        const bool valid = w < words;
+        float v[EPW];
+        read_tagged_strided<EPW>(src + w, stride, valid, v, tag, ok_all);
+        prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
+      }
     }
   };
   // completion: once every wave has issued its h stores, one tagged flag, written
