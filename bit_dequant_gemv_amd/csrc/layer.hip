@@ -150,6 +150,41 @@ __device__ __forceinline__ LayerPtrs ptrs_of(const LayerArgs& A) {
 }
 
 
+// The 2-bit planes of half a code word: thread t takes word t >> 1 and half
+// h = t & 1, i.e. the 8 values that meet the codes of that half (elements 2k + h,
+// k < 8); the planes and scale are those prep_x_word<2> builds for the whole word.
+// A chunk (4 words x 2 halves) is 8 consecutive lanes, aligned to 8, and all 8
+// must call this together.  Twice the threads of prep_x_word<2>, half the work
+// each.
+__device__ __forceinline__ void prep_x_half2(const float (&v)[8], bool valid, int t, uint32_t* planes,
+                                             float* scl, float* xsum) {
+  float m = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                  fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+  float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  // the chunk's 8 lanes: two DPP quads, joined by the half-row mirror
+  m = fmaxf(m, dpp_f<kDppXor1>(m));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+  s += dpp_f<kDppXor1>(s);
+  s += dpp_f<kDppXor2>(s);
+  s += dpp_f<kDppHalfMirror>(s);
+  float f, scale;
+  chunk_exp(m, f, scale);
+  if (valid) {
+    uint32_t u[8], p[6];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) u[k] = to_u24(v[k], f);
+    nibble_planes8(u, p);
+    const int w = t >> 1, h = t & 1, c = w >> 2, i = w & 3;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) planes[c * QTraits<2>::PW + i * 12 + h * 6 + d] = p[d];
+    if (i == 0 && h == 0) {
+      scl[c] = scale * QTraits<2>::FACTOR;
+      xsum[c] = s;
+    }
+  }
+}
+
 __device__ __forceinline__ float bf16_chunk_dot(const uint4 c, const float* xr) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float a0 = 0.f, a1 = 0.f;
