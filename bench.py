@@ -873,6 +873,9 @@ def main():
     ap.add_argument("--phase-probe", action="store_true",
                     help="configs 1/2: load the instrumented library (build.py --probe) and print the "
                          "fused layer's phase timeline instead of the benchmark line")
+    ap.add_argument("--no-device-info", action="store_true",
+                    help="skip the rocminfo / rocm-smi child processes (for runs under a profiler, "
+                         "whose preloaded library has initialised the GPU before this process starts)")
     args = ap.parse_args()
     if args.phase_probe:
         os.environ["QMOE_LIBRARY"] = "probe"
@@ -881,7 +884,7 @@ def main():
               "sharding of this path is a design note, not a measured configuration.", file=sys.stderr)
         sys.exit(2)
 
-    dev_info = device_info()
+    dev_info = {} if args.no_device_info else device_info()
     import torch
     import bit_dequant_gemv_amd as q
     import synth
