@@ -323,6 +323,9 @@ def _check_layer_token(D, x, out, idx, w, residual=None):
 LAYER_CASES = [  # (E, H, I, bits, K)  -- fused shapes, plus shapes served by the fallback chain
     (64, 1024, 256, 4, 4), (64, 1024, 256, 2, 4), (100, 2048, 512, 4, 3), (33, 1024, 512, 4, 1),
     (16, 192, 128, 4, 2), (512, 4096, 1024, 4, 8),
+    # 2-bit planes built from half code words: routed h of 3 and 1 experts (192 and 64
+    # half words, whole waves), and a 2048-wide x (256 half words)
+    (100, 2048, 512, 2, 3), (33, 1024, 512, 2, 1),
 ]
 
 
