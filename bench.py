@@ -589,8 +589,12 @@ def run_stack_bench(args, torch, q, synth):
             "unit": "GB/s", "frac": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": traffic_from_profiles("k_layer_w4_stack60")}
     kern = ("k_stack, 32 + 28 layers per launch" if args.persistent else "k_layer x60 per token")
+    eb = (K + 1) * expert_bytes(4)  # the 5 experts' weight bytes of one layer
     extra = {"kernel": kern + ", RMSNorm fused (roofline per layer launch; traffic per launch)",
              "bytes_per_token": per_tok, "layer_evals_per_s": round(tok_s * n_layers, 1),
+             "expert_bytes_per_layer": eb,
+             # the expert GEMVs' weight bytes over the layer launch that reads them
+             "expert_gemv_GBps_in_layer": round(eb * tok_s * n_layers / 1e9, 1),
              "resident_GB": round(sum(W.routed.buf.numel() + W.shared.buf.numel() for W in layers) / 1e9, 1)}
     cpu = None
     if not args.no_cpu_baseline:
