@@ -64,6 +64,9 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
   static_assert(kFR % RPWI == 0 && DITEMS <= kFW, "one down item per wave at most");
   constexpr int NSP = I / RPWH;            // gate/up items
   constexpr int PW = QTraits<BITS>::PW;
+  // plane words per chunk as kept in LDS: 16 bytes of padding per chunk, so that the
+  // 16-byte reads of consecutive lanes (one chunk each) fall in different banks
+  constexpr int PWL = PW + 4;
 
   constexpr int NB = H / kFR;              // the grid (the host launches exactly this)
   static_assert(I <= H, "a workgroup's h words fit one line");
@@ -76,9 +79,9 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
   const int gli = lane % LGI, subi = lane / LGI;
   const int row0 = wg * kFR;
 
-  __shared__ uint32_t s_xp[CH * PW];
+  __shared__ __align__(16) uint32_t s_xp[CH * PWL];
   __shared__ float s_xsc[CH], s_xsum[CH];
-  __shared__ __align__(16) uint32_t s_hp[CI * PW];
+  __shared__ __align__(16) uint32_t s_hp[CI * PWL];
   __shared__ float s_hsc[CI], s_hsum[CI];
   bool ok = true;
 
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
 
   // ---- 2. x planes, built from registers into LDS (once per workgroup), then in
   //         every wave's registers
-  if (wv * 64 < H / EPW) prep_x_word<BITS>(xv, xvalid, tx, s_xp, s_xsc, s_xsum);
+  if (wv * 64 < H / EPW) prep_x_word<BITS, PWL>(xv, xvalid, tx, s_xp, s_xsc, s_xsum);
   __syncthreads();
-  dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
+  dH.template load_prepped<PWL>(s_xp, s_xsc, s_xsum, CH, glh);
   // tag 0 is what a zero-filled workspace holds: skipped when the counter wraps
   uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)epoch) + 1u;
   tag = tag ? tag : 1u;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
     const bool valid = tx < I / EPW;
     float v[EPW];
     read_tagged_strided<EPW>(hb + (tx / SPW) * kLine + tx % SPW, Q * kLine, valid, v, tag, ok);
-    prep_x_word<BITS>(v, valid, tx, s_hp, s_hsc, s_hsum);
+    prep_x_word<BITS, PWL>(v, valid, tx, s_hp, s_hsc, s_hsum);
   }
   __syncthreads();
   // Every workgroup read the counter before storing its h (each stores at least
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kFB, 2) void k_ffn1(Ffn1Args A) {
     __hip_atomic_store(A.ctrl + CTRL_EPOCH, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (wv < DITEMS) {
     RowDot<BITS, LGI, 1> dD;
-    dD.load_prepped(s_hp, s_hsc, s_hsum, CI, gli);
+    dD.template load_prepped<PWL>(s_hp, s_hsc, s_hsum, CI, gli);
     const uint4 qd[1][1] = {{dq}};
     const uint32_t sd[1][1] = {{dsc}};
     float p[1];

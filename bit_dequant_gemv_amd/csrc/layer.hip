@@ -156,6 +156,7 @@ __device__ __forceinline__ LayerPtrs ptrs_of(const LayerArgs& A) {
 // A chunk (4 words x 2 halves) is 8 consecutive lanes, aligned to 8, and all 8
 // must call this together.  Twice the threads of prep_x_word<2>, half the work
 // each.
+template <int STRIDE>
 __device__ __forceinline__ void prep_x_half2(const float (&v)[8], bool valid, int t, uint32_t* planes,
                                              float* scl, float* xsum) {
   float m = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
@@ -177,7 +178,7 @@ __device__ __forceinline__ void prep_x_half2(const float (&v)[8], bool valid, in
     nibble_planes8(u, p);
     const int w = t >> 1, h = t & 1, c = w >> 2, i = w & 3;
 #pragma unroll
-    for (int d = 0; d < 6; ++d) planes[c * QTraits<2>::PW + i * 12 + h * 6 + d] = p[d];
+    for (int d = 0; d < 6; ++d) planes[c * STRIDE + i * 12 + h * 6 + d] = p[d];
     if (i == 0 && h == 0) {
       scl[c] = scale * QTraits<2>::FACTOR;
       xsum[c] = s;
@@ -221,6 +222,9 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   constexpr int CRQ = H / 32;                   // 16-byte router chunks per quarter row
   constexpr int CPLR = (CRQ + 63) / 64;
   constexpr int PW = QTraits<BITS>::PW;
+  // plane words per chunk as kept in LDS: 16 bytes of padding per chunk, so that the
+  // 16-byte reads of consecutive lanes (one chunk each) fall in different banks
+  constexpr int PWL = PW + 4;
   constexpr int PER_L = (kFusedMaxE + kLB - 1) / kLB;
 
   const int NB = gridDim.x, wg = blockIdx.x;
@@ -237,9 +241,9 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   const int row0 = wg * kRB;
 
   __shared__ __align__(16) float s_x[H];          // the layer input x
-  __shared__ uint32_t s_xp[CH * PW];
+  __shared__ __align__(16) uint32_t s_xp[CH * PWL];
   __shared__ float s_xsc[CH], s_xsum[CH];
-  __shared__ __align__(16) uint32_t s_hp[(kFusedMaxK + 1) * CI * PW];  // their planes
+  __shared__ __align__(16) uint32_t s_hp[(kFusedMaxK + 1) * CI * PWL];  // their planes
   __shared__ float s_hsc[(kFusedMaxK + 1) * CI], s_hsum[(kFusedMaxK + 1) * CI];
   __shared__ float s_y[kFusedMaxK + 1][kRB];
   __shared__ float s_part[kLW];
@@ -433,10 +437,10 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
       float vz[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) vz[k] = valid ? v[k] : 0.f;
-      prep_x_half2(vz, valid, t, s_xp, s_xsc, s_xsum);
+      prep_x_half2<PWL>(vz, valid, t, s_xp, s_xsc, s_xsum);
     }
   } else {
-    prep_x_coop<BITS>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
+    prep_x_coop<BITS, PWL>(s_x, H, s_xp, s_xsc, s_xsum, tx, kLB);
   }
   if (tx == 0) {
     s_tag = tag0;
@@ -468,7 +472,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     if (j) lraw[j] = 0;  // tag 0 is never current: polled in the loop
     if ((int)tx + j * kLB < E) pending |= 1u << j;
   }
-  dH.load_prepped(s_xp, s_xsc, s_xsum, CH, glh);
+  dH.template load_prepped<PWL>(s_xp, s_xsc, s_xsum, CH, glh);
   float hs_val = 0.f;
   QMOE_PT(4);
   // ---- 5. top-K.  Order: larger logit, then lower index; the keys are the
@@ -690,7 +694,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
         const bool valid = t < halves;
         float v[8];
         read_tagged_strided<8>(src + (t & 1) * stride + (t >> 1), 2 * stride, valid, v, tag, ok_all);
-        prep_x_half2(v, valid, t, planes, scl, xsum);
+        prep_x_half2<PWL>(v, valid, t, planes, scl, xsum);
       }
     } else {
       constexpr int EPW = QTraits<BITS>::EPW;
@@ -701,7 +705,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
         const bool valid = w < words;
         float v[EPW];
         read_tagged_strided<EPW>(src + w, stride, valid, v, tag, ok_all);
-        prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
+        prep_x_word<BITS, PWL>(v, valid, w, planes, scl, xsum);
       }
     }
   };
@@ -721,14 +725,14 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   //         and gamma's dot then run before the wait for the routed h, not after it
   //         (measured: 14.91 against 15.28 us per layer, 2-bit 14.16 against 14.72;
   //         the routed planes then also fit one pass of the workgroup's threads).
-  h_planes(hs, kHsW, I, s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI);
+  h_planes(hs, kHsW, I, s_hp + K * CI * PWL, s_hsc + K * CI, s_hsum + K * CI);
   __syncthreads();
   // (a thread past H/8 holds a copy of the last chunk: it adds nothing)
   const float gpart = group_sum_last<64>((int)tx < H / 8 ? bf16_chunk_dot(gq, gx) : 0.f);
   if (lane == 63) s_rv[wv] = gpart;
   if (wv < DITEMS) {  // the wave's shared down item
     RowDot<BITS, LGI, 1> dS;
-    dS.load_prepped(s_hp + K * CI * PW, s_hsc + K * CI, s_hsum + K * CI, CI, gli);
+    dS.template load_prepped<PWL>(s_hp + K * CI * PWL, s_hsc + K * CI, s_hsum + K * CI, CI, gli);
     const uint4 qs[1][1] = {{dq[0]}};
     const uint32_t ss[1][1] = {{dsc[0]}};
     float ps[1];
@@ -773,7 +777,7 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
   const int kw = (wv * MAXR) / DITEMS;
   if (kw < K) {
     RowDot<BITS, LGI, 1> dR;
-    dR.load_prepped(s_hp + kw * CI * PW, s_hsc + kw * CI, s_hsum + kw * CI, CI, gli);
+    dR.template load_prepped<PWL>(s_hp + kw * CI * PWL, s_hsc + kw * CI, s_hsum + kw * CI, CI, gli);
     uint4 qr[MAXR][1];
     uint32_t sr[MAXR][1];
 #pragma unroll

@@ -313,7 +313,7 @@ __device__ __forceinline__ float chunk_dot<2>(const uint4 c, const uint32_t* P) 
 // The planes of word w (EPW values v, zeros when !valid) of an input vector, the
 // chunk scale and the chunk sum: lanes w..w+3 of one DPP quad hold the 4 words of
 // a chunk, and all four must call this together.
-template <int BITS>
+template <int BITS, int STRIDE = QTraits<BITS>::PW>
 __device__ __forceinline__ void prep_x_word(const float (&v)[QTraits<BITS>::EPW], bool valid, int w,
                                             uint32_t* planes, float* scl, float* xsum) {
   constexpr int EPW = QTraits<BITS>::EPW;
@@ -336,7 +336,7 @@ __device__ __forceinline__ void prep_x_word(const float (&v)[QTraits<BITS>::EPW]
     prep_word<BITS>(v, f, p);
     const int c = w >> 2, i = w & 3;
 #pragma unroll
-    for (int k = 0; k < NPW; ++k) planes[c * QTraits<BITS>::PW + i * NPW + k] = p[k];
+    for (int k = 0; k < NPW; ++k) planes[c * STRIDE + i * NPW + k] = p[k];
     if (i == 0) {
       scl[c] = scale * QTraits<BITS>::FACTOR;
       xsum[c] = s;
@@ -348,7 +348,7 @@ __device__ __forceinline__ void prep_x_word(const float (&v)[QTraits<BITS>::EPW]
 // shared memory: planes[c*PW ...], scl[c] (chunk scale, 2-bit 1/4 included) and
 // xsum[c] (plain sum of the chunk's x) for chunks c < n/EPC.  Every thread of the
 // workgroup must call it (shuffles inside); nthreads a multiple of 64.
-template <int BITS>
+template <int BITS, int STRIDE = QTraits<BITS>::PW>
 __device__ __forceinline__ void prep_x_coop(const float* x, int n, uint32_t* planes, float* scl,
                                             float* xsum, int tid, int nthreads) {
   constexpr int EPW = QTraits<BITS>::EPW;
@@ -366,7 +366,7 @@ __device__ __forceinline__ void prep_x_coop(const float* x, int n, uint32_t* pla
       v[j + 2] = f4.z;
       v[j + 3] = f4.w;
     }
-    prep_x_word<BITS>(v, valid, w, planes, scl, xsum);
+    prep_x_word<BITS, STRIDE>(v, valid, w, planes, scl, xsum);
   }
 }
 
@@ -523,13 +523,14 @@ struct RowDot {
   }
 
   // planes prepared by prep_x_coop (shared or global memory)
+  template <int STRIDE = PW>
   __device__ __forceinline__ void load_prepped(const uint32_t* planes, const float* scl,
                                                const float* xsum, int C, int gl) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = gl + i * LG;
       if (c < C) {
-        const uint4* p = reinterpret_cast<const uint4*>(planes + c * PW);
+        const uint4* p = reinterpret_cast<const uint4*>(planes + c * STRIDE);
 #pragma unroll
         for (int k = 0; k < PW / 4; ++k) {
           const uint4 v = p[k];
