@@ -589,8 +589,8 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
 #pragma unroll
     for (int k = 0; k < kFusedMaxK; ++k)
       if (k < K) {
-        Lp.idx_out[k] = eidx[k];
-        Lp.w_out[k] = wsel[k];
+        __hip_atomic_store(Lp.idx_out + k, eidx[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(Lp.w_out + k, wsel[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
   }
 
@@ -814,16 +814,19 @@ __device__ __forceinline__ void layer_body(const LayerArgs& A, const Args& P) {
     for (int k = 0; k < kFusedMaxK; ++k)
       if (k < K) acc = fmaf(wsel[k], s_y[k][tx], acc);
     const float v = fmaf(sigmoid_f(gs), s_y[kFusedMaxK][tx], acc);
+    // the output is written through to memory (agent-scope stores, as the tagged
+    // words are), so the end of the launch finds no dirty L2 lines to write back
+    // (measured: 13.99 -> 13.96 us per layer, 2-bit 12.53 -> 12.44)
     if constexpr (STACK) {
       if (P.h_all) P.h_all[(int64_t)l * H + row0 + tx] = v;
       if (l + 1 < P.nl) {  // the workgroup's rows fill one line: a single writer
         tag_put(P.xbuf + ((int64_t)l * NB + wg) * kLine + tx, v, tag);
         resid = v;
       } else {
-        A.out[row0 + tx] = v;
+        __hip_atomic_store(A.out + row0 + tx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
-      A.out[row0 + tx] = v;
+      __hip_atomic_store(A.out + row0 + tx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if constexpr (!STACK) {
